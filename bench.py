@@ -1,0 +1,306 @@
+#!/usr/bin/env python3
+"""Benchmark of the ReSA hot path on one MI355X.
+
+A step is one pass of the whole hot path over the batch: append + descriptor
+update, GBSA selection, sparse decode, and, after every f-th step, the dense
+rectification of the f newest tokens (so the step rate is amortised over the
+rectification). Inputs are seeded synthetic tensors already resident in HBM.
+
+Prints ONE JSON line. Default workload: batch 4, 32 query / 8 KV heads,
+head_dim 128, bf16, 128K-token prefill, block 16, r = 0.1, n_min = 16, f = 32.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                  [--no-cpu-baseline] [--cpu-seconds S]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GBSA decode steps/s + achieved HBM GB/s at 128K ctx (32q/8kv, d=128)"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+BREAKDOWN_STEPS = 32
+
+
+def _workloads():
+    from block_sparse_attention_quest_amd import workloads as W
+    return {"gqa_128k": W.gqa_128k, "llama8b_32k": W.llama8b_32k, "long_256k": W.long_256k,
+            "tiny_fp32": W.tiny_fp32}
+
+
+# ---------------------------------------------------------------------------
+# Algorithmic bytes / flops (what the method must move; Eq. 6 accounting)
+# ---------------------------------------------------------------------------
+
+def step_bytes(w, L_list, n_list):
+    """Algorithmic HBM bytes of one decode step at sequence lengths L_list (new
+    token included) with n_list selected blocks per sequence."""
+    e = 2 if w.dtype == "bf16" else 4
+    d, Hkv, Hq = w.head_dim, w.num_kv_heads, w.num_q_heads
+    append = desc = sel = 0
+    for L, n in zip(L_list, n_list):
+        M = -(-L // 16)
+        valid_last = L - 16 * (M - 1)
+        # append: the new K/V row, the block's K rows read, its descriptor written
+        append += Hkv * (2 * d * e + valid_last * d * e + 2 * d * e)
+        desc += Hkv * M * 2 * d * e
+        # selected tokens of every group (the newest block is always selected)
+        tokens = 16 * n - (16 - valid_last)
+        sel += Hkv * tokens * 2 * d * e
+    qo = w.batch * Hq * d * e * 2  # q read by select and by decode; out written
+    return {"append": append, "select": desc + w.batch * Hq * d * e,
+            "decode": sel + qo, "selected_kv": sel, "descriptors": desc}
+
+
+def rectify_work(w, L_list, f):
+    e = 2 if w.dtype == "bf16" else 4
+    d, Hkv, Hq = w.head_dim, w.num_kv_heads, w.num_q_heads
+    kv = sum(Hkv * L * 2 * d * e for L in L_list)
+    flops = sum(4 * d * Hq * (f * (L - f) + f * (f + 1) // 2) for L in L_list)
+    return kv, flops
+
+
+def n_for(M, w):
+    return min(M, max(w.n_min, math.ceil(float(M) * float(w.r))))
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands, on a bounded sample of the workload
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(w, first_step, budget_s):
+    import numpy as np
+    import torch
+    from block_sparse_attention_quest_amd import workloads as W
+    from oracle import resa_oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    G, d = w.group, w.head_dim
+    scale = 1.0 / math.sqrt(d)
+    groups = [(b, g) for b in range(w.batch) for g in range(w.num_kv_heads)]
+    rng = np.random.default_rng(0)
+    rng.shuffle(groups)
+    t_dec, t_row = [], []
+    t0 = time.perf_counter()
+    q_all = W.query(w, first_step).double().numpy()
+    for (b, g) in groups:
+        k0, v0 = W.prefill_kv(w, b, g)
+        ks = [k0.double().numpy()]
+        vs = [v0.double().numpy()]
+        for t in range(first_step + 1):
+            k, v = W.append_kv(w, t)
+            ks.append(k[b, g][None].double().numpy())
+            vs.append(v[b, g][None].double().numpy())
+        K = np.concatenate(ks)
+        V = np.concatenate(vs)
+        kmin, kmax = O.block_descriptors(K[:-1]) if len(K) > 1 else (None, None)
+        qg = q_all[b, g * G:(g + 1) * G]
+        M = O.num_blocks(len(K))
+        # one decode step of this group: append's block descriptor, scoring, selection, decode
+        s0 = time.perf_counter()
+        last = (M - 1) * 16
+        lmin, lmax = O.block_descriptors(K[last:])
+        if kmin is not None and len(kmin) == M:
+            kmin[-1], kmax[-1] = lmin[0], lmax[0]
+        else:
+            kmin = np.concatenate([kmin, lmin]) if kmin is not None else lmin
+            kmax = np.concatenate([kmax, lmax]) if kmax is not None else lmax
+        s = O.block_upper_bounds(O.pooled_query(qg), kmin, kmax)
+        sel = O.select_blocks(s, O.active_block_count(M, w.n_min, w.r), w.n_local)
+        O.sparse_decode_group(qg, K, V, sel, scale)
+        t_dec.append(time.perf_counter() - s0)
+        # rectification rows of this group, each over the full cache
+        if w.f > 0 and len(t_row) < 4:
+            for i in range(2):
+                s1 = time.perf_counter()
+                O.causal_rows(qg[i:i + 1], K, V, len(K) - 1, scale)
+                t_row.append(time.perf_counter() - s1)
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dec = float(np.mean(t_dec))
+    row = float(np.mean(t_row)) if t_row else 0.0
+    # per step: every group decodes once; every f steps B * f * Hq rows are rectified
+    sec_per_step = w.batch * w.num_kv_heads * dec + (w.batch * w.num_q_heads * row if w.f > 0 else 0.0)
+    return {"value": 1.0 / sec_per_step, "unit": "steps/s", "cores": int(cores), "kind": "oracle",
+            "sample": (f"{len(t_dec)} of {w.batch * w.num_kv_heads} (sequence, KV-head) groups of one decode step "
+                       f"and {len(t_row)} rectified query rows over the full context, timed on the host in float64 "
+                       f"NumPy and scaled to the whole batch ({dec * 1e3:.1f} ms per group step, "
+                       f"{row * 1e3:.1f} ms per rectified row)")}
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--workload", default="gqa_128k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the hot path here is the per-GPU kernel; "
+              "sharding across GPUs is a design note, not built. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from block_sparse_attention_quest_amd import resa as R
+    from block_sparse_attention_quest_amd import workloads as W
+    from block_sparse_attention_quest_amd.schedule import ResaRunner
+
+    torch.cuda.set_device(0)
+    K, Wu = args.steps, args.warmup
+    base = _workloads()[args.workload]()
+    w = base.replace(steps=Wu + K + BREAKDOWN_STEPS)
+    t_setup = time.perf_counter()
+    print(f"[bench] setting up {w.name}: batch {w.batch}, prefill {w.prefill_lens[0]}, steps {w.steps}",
+          file=sys.stderr, flush=True)
+    r = ResaRunner(w)
+    r.fill_prefill()
+    r.build_descriptors()
+    rect_steps = [t for t in range(w.steps) if w.f > 0 and (t + 1) % w.f == 0]
+    rect_in = {t: tuple(x.cuda() for x in W.rectify_inputs(w, t)) for t in rect_steps}
+    torch.cuda.synchronize()
+    print(f"[bench] setup {time.perf_counter() - t_setup:.1f}s", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+
+    def step(t, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        r.decode_step(t)
+        if ev is not None:
+            ev[1].record(stream)
+        if t in rect_in:
+            r.rectify(t, *rect_in[t])
+
+    for t in range(Wu):
+        step(t)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K whole steps, decode launches bracketed by events ----
+    dec_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    sel_ev = []
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(K):
+        t = Wu + i
+        r.set_step_lens(t + 1)
+        q = r.step_inputs["q"][t]
+        R.resa_update_descriptors(r.cache, r.step_inputs["k"][t], r.step_inputs["v"][t], 1)
+        a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        R.resa_select_blocks(r.cache, q, r.params, r.idx, r.count, r.n_cap, r.ws)
+        b_.record(stream)
+        sel_ev.append((a, b_))
+        dec_ev[i][0].record(stream)
+        R.resa_sparse_decode(r.cache, q, r.idx, r.count, r.n_cap, r.out, r.ws, r.scale)
+        dec_ev[i][1].record(stream)
+        if t in rect_in:
+            r.rectify(t, *rect_in[t])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = e0.elapsed_time(e1)
+    ms_per_step = total_ms / K
+    dec_ms = sum(x.elapsed_time(y) for x, y in dec_ev) / K
+    sel_ms = sum(x.elapsed_time(y) for x, y in sel_ev) / K
+
+    # ---- stage breakdown (after the timed region) ----
+    times = {"append": [], "select": [], "decode": [], "rectify": []}
+    for i in range(BREAKDOWN_STEPS):
+        t = Wu + K + i
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        r.set_step_lens(t + 1)
+        q = r.step_inputs["q"][t]
+        ev[0].record(stream)
+        R.resa_update_descriptors(r.cache, r.step_inputs["k"][t], r.step_inputs["v"][t], 1)
+        ev[1].record(stream)
+        R.resa_select_blocks(r.cache, q, r.params, r.idx, r.count, r.n_cap, r.ws)
+        ev[2].record(stream)
+        R.resa_sparse_decode(r.cache, q, r.idx, r.count, r.n_cap, r.out, r.ws, r.scale)
+        ev[3].record(stream)
+        rev = None
+        if t in rect_in:
+            rev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            rev[0].record(stream)
+            r.rectify(t, *rect_in[t])
+            rev[1].record(stream)
+        torch.cuda.synchronize()
+        times["append"].append(ev[0].elapsed_time(ev[1]))
+        times["select"].append(ev[1].elapsed_time(ev[2]))
+        times["decode"].append(ev[2].elapsed_time(ev[3]))
+        if rev is not None:
+            times["rectify"].append(rev[0].elapsed_time(rev[1]))
+    stage_us = {k: (1e3 * sum(v) / len(v) if v else None) for k, v in times.items()}
+
+    # ---- algorithmic work at the middle of the timed region ----
+    tm = Wu + K // 2
+    L_list = [L + tm + 1 for L in w.prefill_lens]
+    n_list = [n_for(-(-L // 16), w) for L in L_list]
+    sb = step_bytes(w, L_list, n_list)
+    rkv, rflops = rectify_work(w, L_list, w.f) if w.f > 0 else (0, 0)
+    full_cache = sum(w.num_kv_heads * L * 2 * w.head_dim * (2 if w.dtype == "bf16" else 4) for L in L_list)
+    step_alg = sb["append"] + sb["select"] + sb["decode"] + (rkv / w.f if w.f > 0 else 0)
+    dec_gbs = sb["decode"] / (dec_ms * 1e-3) / 1e9
+    sel_gbs = sb["select"] / (sel_ms * 1e-3) / 1e9
+    rect_us = stage_us["rectify"]
+    rect_tflops = (rflops / (rect_us * 1e-6) / 1e12) if rect_us else None
+    rect_gbs = (rkv / (rect_us * 1e-6) / 1e9) if rect_us else None
+
+    result = {
+        "metric": METRIC,
+        "value": round(1e3 / ms_per_step, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wu,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "prefill": w.prefill_lens[0], "q_heads": w.num_q_heads,
+                   "kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block": 16, "r": w.r, "n_min": w.n_min,
+                   "n_local": w.n_local, "f": w.f, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "resa_sparse_decode (k_decode_split + k_decode_combine)",
+                     "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "alg_bytes_per_launch": sb["decode"], "avg_launch_us": round(dec_ms * 1e3, 2)},
+        "hbm_gbs_step": round(step_alg / (ms_per_step * 1e-3) / 1e9, 1),
+        "alg_bytes_per_step": int(step_alg),
+        "eq6_fraction": round(step_alg / full_cache, 5),
+        "selected_kv_bytes_per_group": sb["selected_kv"] / (w.batch * w.num_kv_heads),
+        "full_kv_bytes_per_group": full_cache / (w.batch * w.num_kv_heads),
+        "stages_us": {k: (round(v, 2) if v is not None else None) for k, v in stage_us.items()},
+        "select_gbs": round(sel_gbs, 1),
+        "decode_gbs": round(dec_gbs, 1),
+        "sparse_steps_per_s": round(1e6 / (stage_us["append"] + stage_us["select"] + stage_us["decode"]), 1),
+        "rectify": {"us": rect_us and round(rect_us, 1), "tflops": rect_tflops and round(rect_tflops, 1),
+                    "mfma_frac": rect_tflops and round(rect_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "gbs": rect_gbs and round(rect_gbs, 1)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, tm, args.cpu_seconds)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

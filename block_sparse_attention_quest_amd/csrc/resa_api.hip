@@ -1,0 +1,179 @@
+// C ABI of libresa.so: argument validation, workspace sizing and launch order.
+// All checks run on the host before anything is launched; nothing here reads
+// device memory or synchronises with the device.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "resa_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+resa_status fail(resa_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+resa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return RESA_OK;
+  return fail(RESA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+resa_status check_cache(const resa_cache* c, resa::CacheView* v) {
+  if (!c) return fail(RESA_ERR_INVALID, "cache is NULL");
+  if (c->dtype != RESA_FP32 && c->dtype != RESA_BF16) return fail(RESA_ERR_INVALID, "dtype %d", c->dtype);
+  if (c->batch < 1 || c->num_q_heads < 1 || c->num_kv_heads < 1 || c->head_dim < 1)
+    return fail(RESA_ERR_INVALID, "batch, head counts and head_dim must be positive");
+  if (c->num_q_heads % c->num_kv_heads != 0)
+    return fail(RESA_ERR_INVALID, "num_q_heads %d is not a multiple of num_kv_heads %d", c->num_q_heads,
+                c->num_kv_heads);
+  const int G = c->num_q_heads / c->num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return fail(RESA_ERR_UNSUPPORTED, "group size %d (built: 1, 2, 4, 8)", G);
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(RESA_ERR_UNSUPPORTED, "head_dim %d (built: 64, 128)", c->head_dim);
+  if (c->block_size != resa::kBlock) return fail(RESA_ERR_INVALID, "block_size must be 16, got %d", c->block_size);
+  if (c->num_pages < 1 || c->max_blocks_per_seq < 1 || c->max_seq_len < 1)
+    return fail(RESA_ERR_INVALID, "num_pages, max_blocks_per_seq and max_seq_len must be positive");
+  if ((long)c->max_seq_len > (long)c->max_blocks_per_seq * resa::kBlock)
+    return fail(RESA_ERR_INVALID, "max_seq_len %d exceeds max_blocks_per_seq * 16", c->max_seq_len);
+  if (c->max_blocks_per_seq > resa::kTopnThreads * resa::kTopnMaxPerThread)
+    return fail(RESA_ERR_UNSUPPORTED, "max_blocks_per_seq %d exceeds %d", c->max_blocks_per_seq,
+                resa::kTopnThreads * resa::kTopnMaxPerThread);
+  if ((long)c->num_kv_heads * c->head_dim > 4096)
+    return fail(RESA_ERR_UNSUPPORTED, "num_kv_heads * head_dim exceeds 4096");
+  if (!c->k_pages || !c->v_pages || !c->desc || !c->block_table || !c->seq_lens)
+    return fail(RESA_ERR_INVALID, "cache has a NULL pointer");
+  v->dtype = c->dtype;
+  v->B = c->batch;
+  v->Hq = c->num_q_heads;
+  v->Hkv = c->num_kv_heads;
+  v->D = c->head_dim;
+  v->G = G;
+  v->num_pages = c->num_pages;
+  v->maxb = c->max_blocks_per_seq;
+  v->max_seq_len = c->max_seq_len;
+  v->k = c->k_pages;
+  v->v = c->v_pages;
+  v->kw = c->k_pages;
+  v->vw = c->v_pages;
+  v->desc = c->desc;
+  v->bt = c->block_table;
+  v->seq_lens = c->seq_lens;
+  return RESA_OK;
+}
+
+resa_status check_params(const resa_select_params* p) {
+  if (!p) return fail(RESA_ERR_INVALID, "params is NULL");
+  if (p->n_min < 1) return fail(RESA_ERR_INVALID, "n_min must be >= 1");
+  if (p->n_local < 0) return fail(RESA_ERR_INVALID, "n_local must be >= 0");
+  if (!(p->r > 0.0 && p->r <= 1.0)) return fail(RESA_ERR_INVALID, "r must be in (0, 1]");
+  return RESA_OK;
+}
+
+int n_for(int M, const resa_select_params* p) {
+  int n = (int)ceil((double)M * p->r);
+  if (n < p->n_min) n = p->n_min;
+  return n < M ? n : M;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t resa_n_cap(const resa_cache* cache, const resa_select_params* params) {
+  resa::CacheView v;
+  if (check_cache(cache, &v) != RESA_OK || check_params(params) != RESA_OK) return -1;
+  return n_for((v.max_seq_len + resa::kBlock - 1) / resa::kBlock, params);
+}
+
+size_t resa_select_workspace_size(const resa_cache* cache) {
+  resa::CacheView v;
+  if (check_cache(cache, &v) != RESA_OK) return 0;
+  return size_t(v.B) * v.Hkv * v.maxb * sizeof(double);
+}
+
+size_t resa_decode_workspace_size(const resa_cache* cache, int32_t n_cap) {
+  resa::CacheView v;
+  if (check_cache(cache, &v) != RESA_OK || n_cap < 1) return 0;
+  return resa::decode_ws_bytes(v, n_cap);
+}
+
+size_t resa_rectify_workspace_size(const resa_cache* cache, int32_t f) {
+  resa::CacheView v;
+  if (check_cache(cache, &v) != RESA_OK || f < 1 || f > resa::kMaxRectF) return 0;
+  return resa::rectify_ws_bytes(v, f);
+}
+
+resa_status resa_update_descriptors(const resa_cache* cache, const void* k_new, const void* v_new,
+                                    int32_t n_new, void* stream) {
+  resa::CacheView v;
+  resa_status st = check_cache(cache, &v);
+  if (st != RESA_OK) return st;
+  if (n_new < 0) return fail(RESA_ERR_INVALID, "n_new must be >= 0");
+  if ((k_new == nullptr) != (v_new == nullptr)) return fail(RESA_ERR_INVALID, "k_new and v_new must both be set or both be NULL");
+  if (n_new == 0 && k_new) return fail(RESA_ERR_INVALID, "a rebuild (n_new == 0) takes no new tokens");
+  if (n_new > v.max_seq_len) return fail(RESA_ERR_INVALID, "n_new %d exceeds max_seq_len %d", n_new, v.max_seq_len);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = n_new == 0 ? resa::launch_rebuild(v, s) : resa::launch_update_tail(v, k_new, v_new, n_new, s);
+  return hip_status(e, "resa_update_descriptors");
+}
+
+resa_status resa_select_blocks(const resa_cache* cache, const void* q, const resa_select_params* params,
+                               int32_t* idx, int32_t* count, int32_t n_cap, void* ws, size_t ws_bytes,
+                               void* stream) {
+  resa::CacheView v;
+  resa_status st = check_cache(cache, &v);
+  if (st != RESA_OK) return st;
+  if ((st = check_params(params)) != RESA_OK) return st;
+  if (!q || !idx || !count) return fail(RESA_ERR_INVALID, "q, idx and count must not be NULL");
+  const int need_cap = n_for((v.max_seq_len + resa::kBlock - 1) / resa::kBlock, params);
+  if (n_cap < need_cap) return fail(RESA_ERR_INVALID, "n_cap %d is below resa_n_cap() = %d", n_cap, need_cap);
+  const size_t need = size_t(v.B) * v.Hkv * v.maxb * sizeof(double);
+  if (!ws || ws_bytes < need) return fail(RESA_ERR_WORKSPACE, "select workspace %zu < %zu bytes", ws_bytes, need);
+  return hip_status(resa::launch_select(v, q, *params, idx, count, n_cap, ws, static_cast<hipStream_t>(stream)),
+                    "resa_select_blocks");
+}
+
+resa_status resa_sparse_decode(const resa_cache* cache, const void* q, const int32_t* idx,
+                               const int32_t* count, int32_t n_cap, float scale, void* out, void* ws,
+                               size_t ws_bytes, void* stream) {
+  resa::CacheView v;
+  resa_status st = check_cache(cache, &v);
+  if (st != RESA_OK) return st;
+  if (!q || !idx || !count || !out) return fail(RESA_ERR_INVALID, "q, idx, count and out must not be NULL");
+  if (n_cap < 1 || n_cap > v.maxb) return fail(RESA_ERR_INVALID, "n_cap %d outside 1 .. max_blocks_per_seq", n_cap);
+  if (!(scale > 0.f) || !isfinite(scale)) return fail(RESA_ERR_INVALID, "scale must be positive and finite");
+  const size_t need = resa::decode_ws_bytes(v, n_cap);
+  if (!ws || ws_bytes < need) return fail(RESA_ERR_WORKSPACE, "decode workspace %zu < %zu bytes", ws_bytes, need);
+  return hip_status(resa::launch_decode(v, q, idx, count, n_cap, scale, out, ws, static_cast<hipStream_t>(stream)),
+                    "resa_sparse_decode");
+}
+
+resa_status resa_rectify(const resa_cache* cache, const void* q, const void* k_new, const void* v_new,
+                         int32_t f, float scale, void* out, void* ws, size_t ws_bytes, void* stream) {
+  resa::CacheView v;
+  resa_status st = check_cache(cache, &v);
+  if (st != RESA_OK) return st;
+  if (!q || !k_new || !v_new || !out) return fail(RESA_ERR_INVALID, "q, k_new, v_new and out must not be NULL");
+  if (f < 1 || f > resa::kMaxRectF) return fail(RESA_ERR_UNSUPPORTED, "f %d outside 1 .. %d", f, resa::kMaxRectF);
+  if (f > v.max_seq_len) return fail(RESA_ERR_INVALID, "f %d exceeds max_seq_len %d", f, v.max_seq_len);
+  if (v.dtype == RESA_BF16 && v.G * f > 256)
+    return fail(RESA_ERR_UNSUPPORTED, "group size * f = %d exceeds 256 query rows", v.G * f);
+  if (!(scale > 0.f) || !isfinite(scale)) return fail(RESA_ERR_INVALID, "scale must be positive and finite");
+  const size_t need = resa::rectify_ws_bytes(v, f);
+  if (!ws || ws_bytes < need) return fail(RESA_ERR_WORKSPACE, "rectify workspace %zu < %zu bytes", ws_bytes, need);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // order matters: rectified rows attend to the rectified K/V of earlier rows
+  hipError_t e = resa::launch_update_tail(v, k_new, v_new, f, s);
+  if (e != hipSuccess) return hip_status(e, "resa_rectify (write + refresh)");
+  return hip_status(resa::launch_rectify_attention(v, q, f, scale, out, ws, s), "resa_rectify");
+}
+
+const char* resa_last_error(void) { return g_err; }
+
+}  // extern "C"

@@ -1,0 +1,104 @@
+// Internal declarations shared by the libresa translation units: device helpers,
+// kernel argument blocks and the launchers the C ABI layer calls.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "resa.h"
+
+namespace resa {
+
+constexpr int kBlock = 16;              // tokens per page = selection block
+constexpr int kTopnThreads = 1024;      // one workgroup per (sequence, KV head)
+constexpr int kTopnMaxPerThread = 32;   // => at most 32768 blocks per sequence
+constexpr int kRectTileKeys = 32;       // keys per MFMA key tile
+constexpr int kMaxRectF = 64;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// ---------------------------------------------------------------------------
+// Device helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+// float -> bf16, round to nearest, ties to even (inputs are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+// DPP lane moves (CDNA encodings).
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;   // reverse within each group of 8 lanes
+constexpr int kDppRowMirror = 0x140;    // reverse within each row of 16 lanes
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over each aligned group of 8 lanes; every lane of the group gets the
+// same bits (each step adds a commutative pair).
+__device__ __forceinline__ float sum8(float x) {
+  x += dpp_f32<kDppHalfMirror>(x);
+  x += dpp_f32<kDppQuadXor1>(x);
+  x += dpp_f32<kDppQuadXor2>(x);
+  return x;
+}
+
+__device__ __forceinline__ double shfl_xor_f64(double x, int m) {
+  return __shfl_xor(x, m, 64);
+}
+
+// ---------------------------------------------------------------------------
+// Launchers (one per kernel family; each returns hipGetLastError()).
+// ---------------------------------------------------------------------------
+struct CacheView {
+  int dtype, B, Hq, Hkv, D, G, num_pages, maxb, max_seq_len;
+  const void* k;
+  const void* v;
+  void* kw;   // writable aliases of k / v pages
+  void* vw;
+  void* desc;
+  const int32_t* bt;
+  const int32_t* seq_lens;
+};
+
+hipError_t launch_update_tail(const CacheView& c, const void* k_new, const void* v_new, int n_new,
+                              hipStream_t s);
+hipError_t launch_rebuild(const CacheView& c, hipStream_t s);
+
+hipError_t launch_select(const CacheView& c, const void* q, const resa_select_params& p, int32_t* idx,
+                         int32_t* count, int n_cap, void* ws, hipStream_t s);
+
+struct DecodePlan {
+  int bps;     // selected blocks per split
+  int splits;  // splits per (sequence, KV head)
+};
+DecodePlan plan_decode(const CacheView& c, int n_cap);
+size_t decode_ws_bytes(const CacheView& c, int n_cap);
+hipError_t launch_decode(const CacheView& c, const void* q, const int32_t* idx, const int32_t* count,
+                         int n_cap, float scale, void* out, void* ws, hipStream_t s);
+
+struct RectPlan {
+  int rows;     // G * f query rows per KV head
+  int rows_pad; // rounded up to the row tile
+  int chunk;    // keys per split
+  int splits;   // splits per (sequence, KV head)
+};
+RectPlan plan_rectify(const CacheView& c, int f);
+size_t rectify_ws_bytes(const CacheView& c, int f);
+hipError_t launch_rectify_attention(const CacheView& c, const void* q, int f, float scale, void* out,
+                                    void* ws, hipStream_t s);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace resa

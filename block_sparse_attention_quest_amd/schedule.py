@@ -1,0 +1,136 @@
+"""The ReSA generation schedule on the GPU (host side).
+
+"Rectified Sparse Attention" (abstract; Pith review, "What carries the argument"
+and Figure 2): after prefill the cache descriptors are built once; every decode
+step appends its token (and updates that block's descriptor), selects blocks
+per GQA group and decodes sparsely; after every f-th step the f newest tokens
+are rectified densely. This module only orders the library calls and owns the
+device buffers; every step of the computation runs in libresa's kernels.
+
+Per-step sequence lengths are laid out up front as one small device table, and
+the cache descriptor handed to the library points at the row of the current
+step, so a decode step launches nothing but the library's own kernels.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Optional
+
+import torch
+
+from . import resa as R
+from . import workloads as W
+
+
+class ResaRunner:
+    def __init__(self, w: W.Workload, device="cuda", steps: Optional[int] = None, inputs_on_device: bool = True):
+        self.w = w
+        self.device = device
+        self.steps = w.steps if steps is None else steps
+        B, Hq, Hkv, d = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim
+        self.cache = R.PagedKVCache(B, Hq, Hkv, d, w.num_pages, w.max_blocks_per_seq, w.max_seq_len,
+                                    dtype=w.torch_dtype, device=device)
+        self.block_table_cpu = W.block_table(w)
+        self.cache.block_table.copy_(self.block_table_cpu)
+        # seq_lens of the prefill (row 0) and after each decode step (row t + 1)
+        if self.steps > 0:
+            rows = [[L + t for L in w.prefill_lens] for t in range(self.steps + 1)]
+        else:  # rectify-only workload: row 1 holds the lengths with the f rectified tokens
+            rows = [list(w.prefill_lens), [L + max(w.f, 0) for L in w.prefill_lens]]
+        lens = torch.tensor(rows, dtype=torch.int32)
+        self.lens = lens.to(device)
+        self.params = R.make_params(w.n_min, w.r, w.n_local)
+        self.set_step_lens(0)
+        self.n_cap = R.resa_n_cap(self.cache, self.params)
+        ws = max(R.resa_select_workspace_size(self.cache),
+                 R.resa_decode_workspace_size(self.cache, self.n_cap),
+                 R.resa_rectify_workspace_size(self.cache, w.f) if w.f > 0 else 0)
+        self.ws = R.workspace(ws, device)
+        self.idx = torch.full((B, Hkv, self.n_cap), -1, dtype=torch.int32, device=device)
+        self.count = torch.zeros(B, dtype=torch.int32, device=device)
+        self.out = torch.empty(B, Hq, d, dtype=w.torch_dtype, device=device)
+        self.rect_out = torch.empty(B, max(w.f, 1), Hq, d, dtype=w.torch_dtype, device=device)
+        self.scale = 1.0 / math.sqrt(d)
+        self.step_inputs: Dict[str, torch.Tensor] = {}
+        if inputs_on_device and self.steps > 0:
+            self.step_inputs = {
+                "q": torch.stack([W.query(w, t) for t in range(self.steps)]).to(device),
+                "k": torch.stack([W.append_kv(w, t)[0] for t in range(self.steps)]).unsqueeze(2).to(device),
+                "v": torch.stack([W.append_kv(w, t)[1] for t in range(self.steps)]).unsqueeze(2).to(device),
+            }
+        self.rect_inputs: Dict[int, tuple] = {}
+
+    # -- layout ------------------------------------------------------------
+    def set_step_lens(self, row: int) -> None:
+        """Point the cache descriptor at the sequence lengths after `row` steps."""
+        self.cache.c.seq_lens = self.lens[row].data_ptr()
+        self.cache.seq_lens = self.lens[row]
+
+    def fill_prefill(self) -> None:
+        """Write the seeded prefill K/V into their pages (plumbing, not timed)."""
+        w, c = self.w, self.cache
+        bt = self.block_table_cpu
+        for b in range(w.batch):
+            L = w.prefill_lens[b]
+            M = -(-L // 16)
+            pages = bt[b, :M].to(self.device, torch.long)
+            for h in range(w.num_kv_heads):
+                k, v = W.prefill_kv(w, b, h)
+                pad = M * 16 - L
+                if pad:
+                    k = torch.cat([k, torch.zeros(pad, w.head_dim, dtype=k.dtype)])
+                    v = torch.cat([v, torch.zeros(pad, w.head_dim, dtype=v.dtype)])
+                c.k_pages[pages, h] = k.view(M, 16, w.head_dim).to(self.device)
+                c.v_pages[pages, h] = v.view(M, 16, w.head_dim).to(self.device)
+
+    # -- the hot path -------------------------------------------------------
+    def build_descriptors(self) -> None:
+        self.set_step_lens(0)
+        R.resa_update_descriptors(self.cache, None, None, 0)
+
+    def decode_step(self, t: int, q=None, k=None, v=None) -> torch.Tensor:
+        """Decode step t (0-based): append + descriptor, select, sparse decode."""
+        self.set_step_lens(t + 1)
+        si = self.step_inputs
+        q = si["q"][t] if q is None else q
+        k = si["k"][t] if k is None else k
+        v = si["v"][t] if v is None else v
+        R.resa_update_descriptors(self.cache, k, v, 1)
+        R.resa_select_blocks(self.cache, q, self.params, self.idx, self.count, self.n_cap, self.ws)
+        R.resa_sparse_decode(self.cache, q, self.idx, self.count, self.n_cap, self.out, self.ws, self.scale)
+        return self.out
+
+    def rectify(self, t: int, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, f: Optional[int] = None) -> torch.Tensor:
+        """Rectify the f newest tokens after decode step t (lengths of row t + 1)."""
+        f = self.w.f if f is None else f
+        self.set_step_lens(t + 1)
+        out = self.rect_out[:, :f]
+        if f != self.rect_out.shape[1]:
+            out = torch.empty(self.w.batch, f, self.w.num_q_heads, self.w.head_dim, dtype=self.w.torch_dtype,
+                              device=self.device)
+        R.resa_rectify(self.cache, q, k, v, f, out, self.ws, self.scale)
+        return out
+
+    def rectify_only(self) -> torch.Tensor:
+        """Rectify-only workload: the f newest tokens of every sequence (beyond the
+        prefill) are written, their blocks refreshed, and their rows attended."""
+        q, k, v = (x.to(self.device) for x in W.rectify_only_inputs(self.w))
+        self.rect_inputs[-1] = (q, k, v)
+        return self.rectify(0, q, k, v)
+
+    def rectify_inputs(self, t: int):
+        if t not in self.rect_inputs:
+            self.rect_inputs[t] = tuple(x.to(self.device) for x in W.rectify_inputs(self.w, t))
+        return self.rect_inputs[t]
+
+    def run(self, steps: Optional[int] = None, on_step=None, on_rectify=None) -> None:
+        """The full schedule: every step, then a rectification after each f-th."""
+        steps = self.steps if steps is None else steps
+        for t in range(steps):
+            o = self.decode_step(t)
+            if on_step is not None:
+                on_step(t, o)
+            if self.w.f > 0 and (t + 1) % self.w.f == 0:
+                ro = self.rectify(t, *self.rectify_inputs(t))
+                if on_rectify is not None:
+                    on_rectify(t, ro)

@@ -79,7 +79,8 @@ class Workload:
 
     @property
     def max_seq_len(self) -> int:
-        return max(self.prefill_lens) + self.steps
+        # a rectify-only workload (no decode steps) grows by its f rectified tokens
+        return max(self.prefill_lens) + (self.steps if self.steps > 0 else max(self.f, 0))
 
     @property
     def max_blocks_per_seq(self) -> int:

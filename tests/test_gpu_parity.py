@@ -1,0 +1,169 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, element by
+element, on seeded inputs small enough for the oracle and spanning several
+tiles and ragged tails.
+
+Bars: descriptors bit-exact; selected block sets bit-exact except near-ties
+(oracle score within 1e-6 relative of the threshold); attention outputs within
+1e-4 absolute (fp32) and 2e-2 absolute (bf16); cache rows written by an append
+or a rectification bit-exact.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import resa_oracle as O
+from block_sparse_attention_quest_amd import workloads as W
+
+import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+def _runner(w, steps=None):
+    from block_sparse_attention_quest_amd.schedule import ResaRunner
+    print(f"[case] {w.name} seed={w.seed} B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} d={w.head_dim} "
+          f"prefill={w.prefill_lens[:4]} steps={w.steps if steps is None else steps} f={w.f}", flush=True)
+    r = ResaRunner(w, steps=steps)
+    r.fill_prefill()
+    r.build_descriptors()
+    return r
+
+
+def _run_loop_parity(w, steps=None, check_all_desc_every=0):
+    steps = w.steps if steps is None else steps
+    r = _runner(w, steps)
+    oc = P.oracle_cache(w)
+    torch.cuda.synchronize()
+    P.assert_desc_equal(r.cache.desc, oc)
+    atol = P.ATOL[w.dtype]
+    worst, ties = 0.0, 0
+    for t in range(steps):
+        q, k, v = W.query(w, t), *W.append_kv(w, t)
+        O.append(oc, P.f64(k), P.f64(v))
+        out = r.decode_step(t)
+        torch.cuda.synchronize()
+        # the appended rows and their blocks' descriptors
+        for b in range(w.batch):
+            pos = oc.seq_lens[b] - 1
+            page = int(oc.block_table[b, pos // 16])
+            assert torch.equal(r.cache.k_pages[page, :, pos % 16].cpu(), k[b]), (t, b)
+            assert torch.equal(r.cache.v_pages[page, :, pos % 16].cpu(), v[b]), (t, b)
+            P.assert_desc_equal(r.cache.desc, oc, [page])
+        err, nt = P.check_select_and_decode(oc, P.f64(q), w, r.idx, r.count, out, atol)
+        worst, ties = max(worst, err), ties + nt
+        if w.f > 0 and (t + 1) % w.f == 0:
+            rq, rk, rv = W.rectify_inputs(w, t)
+            ref = O.rectify(oc, P.f64(rq), P.f64(rk), P.f64(rv), 1.0 / math.sqrt(w.head_dim))
+            got = r.rectify(t, rq.cuda(), rk.cuda(), rv.cuda())
+            torch.cuda.synchronize()
+            rerr = np.abs(P.f64(got) - ref).max()
+            assert rerr <= atol, f"rectify error {rerr} at step {t}"
+            worst = max(worst, rerr)
+            # rectified rows are in the cache exactly, descriptors refreshed exactly
+            for b in range(w.batch):
+                L = oc.seq_lens[b]
+                for i in range(w.f):
+                    pos = L - w.f + i
+                    page = int(oc.block_table[b, pos // 16])
+                    assert torch.equal(r.cache.k_pages[page, :, pos % 16].cpu(), rk[b, i])
+                    assert torch.equal(r.cache.v_pages[page, :, pos % 16].cpu(), rv[b, i])
+            P.assert_desc_equal(r.cache.desc, oc)
+        if check_all_desc_every and (t + 1) % check_all_desc_every == 0:
+            P.assert_desc_equal(r.cache.desc, oc)
+    print(f"[result] {w.name}: max abs error {worst:.3g}, near-tie swaps {ties}", flush=True)
+    return worst
+
+
+def test_tiny_fp32_full_schedule():
+    """1024-token fp32 case, one group of 4 heads, d 64: 64 steps, rectify at 32 and 64."""
+    _run_loop_parity(W.tiny_fp32(), check_all_desc_every=16)
+
+
+SMALL = [
+    # name, dtype, B, Hq, Hkv, d, prefill, steps, f, n_min, r, n_local
+    ("bf16_g4_d128", "bf16", 3, 8, 2, 128, (37, 300, 1000), 10, 4, 4, 0.1, 1),
+    ("bf16_g4_d64", "bf16", 2, 8, 2, 64, (129, 777), 9, 3, 4, 0.2, 1),
+    ("bf16_g1_d128", "bf16", 2, 2, 2, 128, (64, 500), 6, 3, 2, 0.1, 1),
+    ("bf16_g2_d128", "bf16", 2, 4, 2, 128, (250, 99), 6, 6, 3, 0.15, 2),
+    ("bf16_g8_d128", "bf16", 1, 16, 2, 128, (2000,), 8, 4, 16, 0.1, 1),
+    ("fp32_g4_d128", "fp32", 2, 8, 2, 128, (333, 64), 8, 4, 4, 0.1, 1),
+    ("bf16_dense_r1", "bf16", 2, 8, 2, 128, (100, 31), 5, 5, 1, 1.0, 1),
+    ("bf16_no_local", "bf16", 2, 8, 2, 128, (600, 17), 6, 3, 4, 0.05, 0),
+    ("bf16_nmin_over_M", "bf16", 2, 8, 2, 128, (40, 200), 4, 2, 64, 0.1, 1),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_schedules(case):
+    name, dt, B, Hq, Hkv, d, pre, steps, f, n_min, r, n_local = case
+    w = W.Workload(name, dt, B, Hq, Hkv, d, pre, steps, f, n_min, r, n_local,
+                   tuple(max(0, min(3, (L // 16) - 1)) for L in pre), dt == "bf16", 100 + len(name))
+    _run_loop_parity(w)
+
+
+def test_single_token_sequences():
+    """A sequence whose only token is the one just appended (M = 1, n = 1)."""
+    w = W.Workload("one_token", "bf16", 3, 8, 2, 128, (0, 15, 16), 3, 0, 4, 0.1, 1, (0, 0, 0), True, 7)
+    _run_loop_parity(w)
+
+
+def test_rectify_whole_sequence_and_ragged_batch():
+    """f equal to the whole length of the shortest sequence; lengths across tiles."""
+    # f = 32 sizes the workspace; four decode steps never reach a scheduled rectification
+    w = W.Workload("rect_all", "bf16", 3, 8, 2, 128, (28, 70, 513), 4, 32, 2, 0.1, 1, (0, 1, 2), True, 8)
+    r = _runner(w)
+    oc = P.oracle_cache(w)
+    for t in range(4):
+        q, k, v = W.query(w, t), *W.append_kv(w, t)
+        O.append(oc, P.f64(k), P.f64(v))
+        r.decode_step(t)
+    for f in (32, 1, 17):   # 32 = the whole first sequence
+        rq, rk, rv = (x[:, :f] for x in _rect_inputs(w, f, seed=f))
+        ref = O.rectify(oc, P.f64(rq), P.f64(rk), P.f64(rv), 1.0 / math.sqrt(w.head_dim))
+        got = r.rectify(3, rq.cuda(), rk.cuda(), rv.cuda(), f=f)
+        torch.cuda.synchronize()
+        err = np.abs(P.f64(got) - ref).max()
+        assert err <= P.ATOL["bf16"], (f, err)
+        P.assert_desc_equal(r.cache.desc, oc)
+
+
+def _rect_inputs(w, f, seed):
+    g = torch.Generator().manual_seed(1000 + seed)
+    q = torch.randn(w.batch, f, w.num_q_heads, w.head_dim, generator=g).to(w.torch_dtype)
+    k = torch.randn(w.batch, f, w.num_kv_heads, w.head_dim, generator=g).to(w.torch_dtype)
+    v = torch.randn(w.batch, f, w.num_kv_heads, w.head_dim, generator=g).to(w.torch_dtype)
+    return q, k, v
+
+
+def test_rectify_mixed_lengths_small():
+    """Mixed-length batch, f = 64, G * f = 256 query rows per KV head (two row tiles per wave)."""
+    w = W.rectify_mixed(batch=4, len_range=(100, 3000), seed=21)
+    r = _runner(w)
+    oc = P.oracle_cache(w)
+    got = r.rectify_only()
+    q, k, v = r.rect_inputs[-1]
+    for b in range(w.batch):
+        oc.seq_lens[b] += w.f
+    ref = O.rectify(oc, P.f64(q), P.f64(k), P.f64(v), 1.0 / math.sqrt(w.head_dim))
+    torch.cuda.synchronize()
+    err = np.abs(P.f64(got) - ref).max()
+    print(f"[result] mixed rectify max abs error {err:.3g}")
+    assert err <= P.ATOL["bf16"]
+    P.assert_desc_equal(r.cache.desc, oc)
+
+
+def test_decode_is_deterministic():
+    w = W.Workload("det", "bf16", 2, 8, 2, 128, (3000, 1234), 3, 0, 16, 0.1, 1, (5, 5), True, 9)
+    outs = []
+    for _ in range(2):
+        r = _runner(w)
+        res = []
+        for t in range(3):
+            res.append(r.decode_step(t).clone())
+            res.append(r.idx.clone())
+        torch.cuda.synchronize()
+        outs.append(res)
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
