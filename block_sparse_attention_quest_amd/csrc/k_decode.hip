@@ -3,52 +3,49 @@
 // its 16-token block is selected), split over the key axis in the manner of
 // Flash-Decoding (reference [6] of the Pith reference list), then merged exactly.
 //
-// k_decode_split: one wave per (sequence, KV head, split). The wave streams one
-// selected block (16 tokens x head_dim of K and of V, 4 KiB each at d=128 bf16)
-// per iteration and serves all G query heads of the group from it, so each
-// selected byte is fetched once per group. Lane layout: lane = 8 * tp + cg; the
-// lane holds tokens tp and tp + 8 and channels cg*8 + 64*k + [0, 8), so every
-// 16-byte load instruction of the wave covers 8 full 128-byte lines. q.k uses
-// v_dot2 on packed bf16 pairs (fp32 accumulate), then a 3-step DPP sum over the
-// 8 lanes sharing the tokens. Each group of 8 lanes keeps its own online-softmax
-// state (running max m, sum l, unnormalised accumulator) over its tokens, so no
-// cross-lane max is needed per block; m is only moved up when a new logit
-// exceeds it by more than 2^8 (the result is unchanged: numerator and
-// denominator share every rescale). At the end the 8 states are merged with
-// log-sum-exp weights and written to the workspace as (m, l, acc[d]) in fp32.
-//
-// k_decode_combine: one wave per (sequence, query head) merges the live splits.
+// k_decode, grid (split, KV head, sequence), 4 waves. A split is a run of the
+// group's selected blocks; wave w takes every 4th of them. Per block the wave
+// reads the K tile (16 tokens x d, token-major) and the V tile (stored
+// channel-major, d x 16 tokens) of one page, 4 KiB each at d = 128 bf16, and
+// serves all G query heads of the group from them, so each selected byte is
+// fetched once per group. The next block's tiles are loaded while the current
+// one is processed.
+//   q.k: lane = 8 * tp + cg holds tokens tp and tp + 8 and channels
+//   cg*8 + 64*k + [0, 8) of K (every 16-byte load covers whole 128-byte lines);
+//   bf16 pairs go through v_dot2 with fp32 accumulation, then a 3-step DPP sum
+//   over the 8 lanes that share the tokens.
+//   softmax: one running max per head for the whole wave, moved only when a
+//   logit exceeds it by more than 2^8 (numerator and denominator share every
+//   rescale, so the result is unchanged); each of the 2G (token, head) pairs of
+//   a token pair is exponentiated by one lane and published through LDS.
+//   p.V: lane owns head_dim/64 channels; its V rows are 16 contiguous tokens.
+// The 4 wave states are merged through LDS into one split partial (m, l,
+// acc[d]) in fp32; k_decode_combine then merges a group's splits with
+// log-sum-exp weights (a separate kernel, so the hand-off needs no
+// device-scope fence).
 #include "resa_internal.h"
 
 namespace resa {
 namespace {
 
 constexpr float kLazyRescale = 8.0f;  // log2 units
+constexpr int kDecWaves = 4;
+constexpr int kDecThreads = 64 * kDecWaves;
 
+// One lane's channels of one K token row.
 template <typename T, int D>
-struct TokenRow;  // one lane's D/8 channels of one token row
-
+struct KRow;
 template <int D>
-struct TokenRow<uint16_t, D> {
-  static constexpr int NCH = D / 64;  // 16-byte chunks per lane
+struct KRow<uint16_t, D> {
+  static constexpr int NCH = D / 64;
   uint4 u[NCH];
   __device__ void load(const uint16_t* row, int cg) {
 #pragma unroll
     for (int k = 0; k < NCH; ++k) u[k] = *reinterpret_cast<const uint4*>(row + cg * 8 + 64 * k);
   }
-  __device__ void zero() {
-#pragma unroll
-    for (int k = 0; k < NCH; ++k) u[k] = make_uint4(0, 0, 0, 0);
-  }
-  __device__ float get(int i) const {  // channel i of the lane's 8*NCH
-    const uint4 w = u[i / 8];
-    const uint32_t x = (i % 8) < 2 ? w.x : (i % 8) < 4 ? w.y : (i % 8) < 6 ? w.z : w.w;
-    return (i & 1) ? bf16_hi(x) : bf16_lo(x);
-  }
 };
-
 template <int D>
-struct TokenRow<float, D> {
+struct KRow<float, D> {
   static constexpr int NCH = D / 64;
   float4 u[NCH][2];
   __device__ void load(const float* row, int cg) {
@@ -59,10 +56,6 @@ struct TokenRow<float, D> {
       u[k][1] = p[1];
     }
   }
-  __device__ void zero() {
-#pragma unroll
-    for (int k = 0; k < NCH; ++k) u[k][0] = u[k][1] = make_float4(0.f, 0.f, 0.f, 0.f);
-  }
   __device__ float get(int i) const {
     const float4 w = u[i / 8][(i % 8) / 4];
     const int r = i % 4;
@@ -70,7 +63,7 @@ struct TokenRow<float, D> {
   }
 };
 
-// The query of one head, restricted to the lane's channels.
+// The query of one head restricted to the lane's K channels.
 template <typename T, int D>
 struct QRow;
 template <int D>
@@ -84,7 +77,7 @@ struct QRow<uint16_t, D> {
       w[4 * k + 0] = u.x; w[4 * k + 1] = u.y; w[4 * k + 2] = u.z; w[4 * k + 3] = u.w;
     }
   }
-  __device__ float dot(const TokenRow<uint16_t, D>& kr) const {
+  __device__ float dot(const KRow<uint16_t, D>& kr) const {
     float s = 0.f;
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
@@ -110,11 +103,77 @@ struct QRow<float, D> {
       w[8 * k + 4] = b.x; w[8 * k + 5] = b.y; w[8 * k + 6] = b.z; w[8 * k + 7] = b.w;
     }
   }
-  __device__ float dot(const TokenRow<float, D>& kr) const {
+  __device__ float dot(const KRow<float, D>& kr) const {
     float s = 0.f;
 #pragma unroll
     for (int i = 0; i < NC; ++i) s = fmaf(w[i], kr.get(i), s);
     return s;
+  }
+};
+
+// One lane's V rows (channel-major page tile): CPL channels x 16 tokens.
+template <typename T, int CPL>
+struct VRows;
+template <int CPL>
+struct VRows<uint16_t, CPL> {
+  uint4 u[CPL][2];  // 16 bf16 tokens per channel
+  __device__ void load(const uint16_t* tile, int lane) {
+#pragma unroll
+    for (int cc = 0; cc < CPL; ++cc) {
+      const uint4* p = reinterpret_cast<const uint4*>(tile + (lane * CPL + cc) * 16);
+      u[cc][0] = p[0];
+      u[cc][1] = p[1];
+    }
+  }
+  __device__ float get(int cc, int t) const {
+    const uint4 w = u[cc][t / 8];
+    const int r = (t % 8) / 2;
+    const uint32_t x = r == 0 ? w.x : r == 1 ? w.y : r == 2 ? w.z : w.w;
+    return (t & 1) ? bf16_hi(x) : bf16_lo(x);
+  }
+  __device__ static uint32_t keep2(uint32_t x, int t0, int valid) {
+    return x & ((t0 < valid ? 0x0000ffffu : 0u) | (t0 + 1 < valid ? 0xffff0000u : 0u));
+  }
+  __device__ void mask_tokens(int valid) {
+#pragma unroll
+    for (int cc = 0; cc < CPL; ++cc)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        uint4& w = u[cc][i];
+        w.x = keep2(w.x, 8 * i + 0, valid);
+        w.y = keep2(w.y, 8 * i + 2, valid);
+        w.z = keep2(w.z, 8 * i + 4, valid);
+        w.w = keep2(w.w, 8 * i + 6, valid);
+      }
+  }
+};
+template <int CPL>
+struct VRows<float, CPL> {
+  float4 u[CPL][4];
+  __device__ void load(const float* tile, int lane) {
+#pragma unroll
+    for (int cc = 0; cc < CPL; ++cc) {
+      const float4* p = reinterpret_cast<const float4*>(tile + (lane * CPL + cc) * 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) u[cc][i] = p[i];
+    }
+  }
+  __device__ float get(int cc, int t) const {
+    const float4 w = u[cc][t / 4];
+    const int r = t % 4;
+    return r == 0 ? w.x : r == 1 ? w.y : r == 2 ? w.z : w.w;
+  }
+  __device__ void mask_tokens(int valid) {
+#pragma unroll
+    for (int cc = 0; cc < CPL; ++cc)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float4& w = u[cc][i];
+        w.x = 4 * i + 0 < valid ? w.x : 0.f;
+        w.y = 4 * i + 1 < valid ? w.y : 0.f;
+        w.z = 4 * i + 2 < valid ? w.z : 0.f;
+        w.w = 4 * i + 3 < valid ? w.w : 0.f;
+      }
   }
 };
 
@@ -125,144 +184,9 @@ struct DecodeArgs {
   const int32_t* count;
   int n_cap, bps, splits;
   float scale_log2;
-  float* part_ml;   // [B][Hq][splits][2]
-  float* part_acc;  // [B][Hq][splits][D]
+  float* part_ml;      // [B*Hkv][splits][G][2]
+  float* part_acc;     // [B*Hkv][splits][G][D]
 };
-
-// grid: x = split, y = KV head, z = sequence; 64 threads.
-template <typename T, int D, int G>
-__global__ __launch_bounds__(64) void k_decode_split(DecodeArgs a) {
-  constexpr int NC = D / 8;  // channels per lane
-  const CacheView& c = a.c;
-  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x, tp = lane >> 3, cg = lane & 7;
-  const int n = a.count[b];
-  const int first = s * a.bps;
-  const int nblk = min(a.bps, n - first);
-  if (nblk <= 0) return;
-  const int L = c.seq_lens[b];
-
-  QRow<T, D> qr[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-    qr[h].load(static_cast<const T*>(a.q) + (size_t(b) * c.Hq + size_t(g) * G + h) * D, cg);
-
-  int my_blk = 0, my_page = 0;
-  if (lane < nblk) {
-    my_blk = a.idx[(size_t(b) * c.Hkv + g) * a.n_cap + first + lane];
-    my_page = c.bt[size_t(b) * c.maxb + my_blk];
-  }
-
-  float m[G], l[G], acc[G][NC];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = -__builtin_inff();
-    l[h] = 0.f;
-#pragma unroll
-    for (int i = 0; i < NC; ++i) acc[h][i] = 0.f;
-  }
-
-  const T* kbase = static_cast<const T*>(c.k);
-  const T* vbase = static_cast<const T*>(c.v);
-  auto row_ptr = [&](const T* base, int page, int t) {
-    return base + ((size_t(page) * c.Hkv + g) * kBlock + t) * D;
-  };
-
-  TokenRow<T, D> k0, k1, v0, v1, nk0, nk1, nv0, nv1;
-  {
-    const int page = __builtin_amdgcn_readlane(my_page, 0);
-    k0.load(row_ptr(kbase, page, tp), cg);
-    k1.load(row_ptr(kbase, page, tp + 8), cg);
-    v0.load(row_ptr(vbase, page, tp), cg);
-    v1.load(row_ptr(vbase, page, tp + 8), cg);
-  }
-  for (int it = 0; it < nblk; ++it) {
-    const int blk = __builtin_amdgcn_readlane(my_blk, it);
-    if (it + 1 < nblk) {  // prefetch the next block
-      const int np = __builtin_amdgcn_readlane(my_page, it + 1);
-      nk0.load(row_ptr(kbase, np, tp), cg);
-      nk1.load(row_ptr(kbase, np, tp + 8), cg);
-      nv0.load(row_ptr(vbase, np, tp), cg);
-      nv1.load(row_ptr(vbase, np, tp + 8), cg);
-    }
-    const int valid = min(kBlock, L - blk * kBlock);
-    const bool ok0 = tp < valid, ok1 = tp + 8 < valid;
-    if (!ok0) { k0.zero(); v0.zero(); }
-    if (!ok1) { k1.zero(); v1.zero(); }
-
-    float x0[G], x1[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      x0[h] = sum8(qr[h].dot(k0)) * a.scale_log2;
-      x1[h] = sum8(qr[h].dot(k1)) * a.scale_log2;
-      if (!ok0) x0[h] = -__builtin_inff();
-      if (!ok1) x1[h] = -__builtin_inff();
-    }
-    bool need = false;
-#pragma unroll
-    for (int h = 0; h < G; ++h) need |= fmaxf(x0[h], x1[h]) > m[h] + kLazyRescale;
-    if (__builtin_amdgcn_ballot_w64(need)) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float cand = fmaxf(x0[h], x1[h]);
-        if (cand > m[h] + kLazyRescale) {
-          const float alpha = m[h] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m[h] - cand);
-          l[h] *= alpha;
-#pragma unroll
-          for (int i = 0; i < NC; ++i) acc[h][i] *= alpha;
-          m[h] = cand;
-        }
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float p0 = ok0 ? __builtin_amdgcn_exp2f(x0[h] - m[h]) : 0.f;
-      const float p1 = ok1 ? __builtin_amdgcn_exp2f(x1[h] - m[h]) : 0.f;
-      l[h] += p0 + p1;
-#pragma unroll
-      for (int i = 0; i < NC; ++i) acc[h][i] = fmaf(p0, v0.get(i), fmaf(p1, v1.get(i), acc[h][i]));
-    }
-    if (it + 1 < nblk) {
-      k0 = nk0; k1 = nk1; v0 = nv0; v1 = nv1;
-    }
-  }
-
-  // merge the 8 token-pair states (lanes differing in bits 3..5)
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float mm = m[h];
-    mm = fmaxf(mm, __shfl_xor(mm, 8, 64));
-    mm = fmaxf(mm, __shfl_xor(mm, 16, 64));
-    mm = fmaxf(mm, __shfl_xor(mm, 32, 64));
-    const float alpha = m[h] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m[h] - mm);
-    float ll = l[h] * alpha;
-    ll += __shfl_xor(ll, 8, 64);
-    ll += __shfl_xor(ll, 16, 64);
-    ll += __shfl_xor(ll, 32, 64);
-#pragma unroll
-    for (int i = 0; i < NC; ++i) {
-      float v = acc[h][i] * alpha;
-      v += __shfl_xor(v, 8, 64);
-      v += __shfl_xor(v, 16, 64);
-      v += __shfl_xor(v, 32, 64);
-      acc[h][i] = v;
-    }
-    const size_t slot = (size_t(b) * c.Hq + size_t(g) * G + h) * a.splits + s;
-    if (tp == h % 8) {
-      float* dst = a.part_acc + slot * D;
-#pragma unroll
-      for (int k = 0; k < D / 64; ++k) {
-        float4* p = reinterpret_cast<float4*>(dst + cg * 8 + 64 * k);
-        p[0] = make_float4(acc[h][8 * k + 0], acc[h][8 * k + 1], acc[h][8 * k + 2], acc[h][8 * k + 3]);
-        p[1] = make_float4(acc[h][8 * k + 4], acc[h][8 * k + 5], acc[h][8 * k + 6], acc[h][8 * k + 7]);
-      }
-      if (cg == 0) {
-        a.part_ml[slot * 2 + 0] = mm;
-        a.part_ml[slot * 2 + 1] = ll;
-      }
-    }
-  }
-}
 
 template <typename T>
 __device__ __forceinline__ void store_out(void* out, size_t i, float x) {
@@ -270,45 +194,228 @@ __device__ __forceinline__ void store_out(void* out, size_t i, float x) {
   else static_cast<float*>(out)[i] = x;
 }
 
-// grid: x = query head, y = sequence; 64 threads.
-template <typename T, int D>
-__global__ __launch_bounds__(64) void k_decode_combine(const float* __restrict__ part_ml,
-                                                       const float* __restrict__ part_acc,
-                                                       const int32_t* __restrict__ count, int Hq,
-                                                       int bps, int splits, void* __restrict__ out) {
-  const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
-  const int live = (count[b] + bps - 1) / bps;
-  const size_t slot0 = (size_t(b) * Hq + h) * splits;
-  float mx = -__builtin_inff();
-  for (int s = lane; s < live; s += 64) mx = fmaxf(mx, part_ml[(slot0 + s) * 2]);
+template <int G, int D>
+struct DecSmem {
+  float p[kDecWaves][16][G];      // probabilities of the current block, per wave
+  float m[kDecWaves][G];
+  float l[kDecWaves][G];
+  float acc[kDecWaves][G][D];
+};
+
+// grid: x = split, y = KV head, z = sequence; 256 threads.
+template <typename T, int D, int G>
+__global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
+  constexpr int CPL = D / 64;                      // V channels per lane
+  constexpr int PAIRS = 2 * G;                     // (token, head) pairs per token pair
+  constexpr int PPL = PAIRS > 8 ? PAIRS / 8 : 1;   // pairs per lane
+  __shared__ DecSmem<G, D> sm;
+  const CacheView& c = a.c;
+  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tp = lane >> 3, cg = lane & 7;
+  const int n = a.count[b];
+  const int first = s * a.bps;
+  const int nblk = min(a.bps, n - first);
+  if (nblk <= 0) return;
+  const int L = c.seq_lens[b];
+  const size_t gi = size_t(b) * c.Hkv + g;
+
+  QRow<T, D> qr[G];
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-  float num[D / 64], den = 0.f;
-#pragma unroll
-  for (int e = 0; e < D / 64; ++e) num[e] = 0.f;
-  for (int s = 0; s < live; ++s) {
-    const float ms = part_ml[(slot0 + s) * 2];
-    const float w = ms == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(ms - mx);
-    den = fmaf(w, part_ml[(slot0 + s) * 2 + 1], den);
-#pragma unroll
-    for (int e = 0; e < D / 64; ++e) num[e] = fmaf(w, part_acc[(slot0 + s) * D + lane + 64 * e], num[e]);
+  for (int h = 0; h < G; ++h)
+    qr[h].load(static_cast<const T*>(a.q) + (size_t(b) * c.Hq + size_t(g) * G + h) * D, cg);
+
+  // this wave's blocks: first + wave + 4 * i
+  const int nw = nblk > wave ? (nblk - wave + kDecWaves - 1) / kDecWaves : 0;
+  int my_blk = 0, my_page = 0;
+  if (lane < nw) {
+    my_blk = a.idx[gi * a.n_cap + first + wave + kDecWaves * lane];
+    my_page = c.bt[size_t(b) * c.maxb + my_blk];
   }
-  const float inv = 1.f / den;
+
+  float m[G], lpart[PPL], acc[G][CPL];
 #pragma unroll
-  for (int e = 0; e < D / 64; ++e)
-    store_out<T>(out, (size_t(b) * Hq + h) * D + lane + 64 * e, num[e] * inv);
+  for (int h = 0; h < G; ++h) {
+    m[h] = -__builtin_inff();
+#pragma unroll
+    for (int cc = 0; cc < CPL; ++cc) acc[h][cc] = 0.f;
+  }
+#pragma unroll
+  for (int u = 0; u < PPL; ++u) lpart[u] = 0.f;
+
+  const T* kbase = static_cast<const T*>(c.k);
+  const T* vbase = static_cast<const T*>(c.v);
+  auto tile = [&](const T* base, int page) { return base + (size_t(page) * c.Hkv + g) * kBlock * D; };
+
+  KRow<T, D> k0, k1, nk0, nk1;
+  VRows<T, CPL> vr, nvr;
+  if (nw > 0) {
+    const int page = __builtin_amdgcn_readlane(my_page, 0);
+    k0.load(tile(kbase, page) + tp * D, cg);
+    k1.load(tile(kbase, page) + (tp + 8) * D, cg);
+    vr.load(tile(vbase, page), lane);
+  }
+  for (int it = 0; it < nw; ++it) {
+    const int blk = __builtin_amdgcn_readlane(my_blk, it);
+    if (it + 1 < nw) {
+      const int np = __builtin_amdgcn_readlane(my_page, it + 1);
+      nk0.load(tile(kbase, np) + tp * D, cg);
+      nk1.load(tile(kbase, np) + (tp + 8) * D, cg);
+      nvr.load(tile(vbase, np), lane);
+    }
+    const int valid = min(kBlock, L - blk * kBlock);
+    const bool ok0 = tp < valid, ok1 = tp + 8 < valid;
+
+    float x0[G], x1[G];
+    bool need = false;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      x0[h] = ok0 ? sum8(qr[h].dot(k0)) * a.scale_log2 : -__builtin_inff();
+      x1[h] = ok1 ? sum8(qr[h].dot(k1)) * a.scale_log2 : -__builtin_inff();
+      need |= fmaxf(x0[h], x1[h]) > m[h] + kLazyRescale;
+    }
+    if (__builtin_amdgcn_ballot_w64(need)) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float bm = fmaxf(x0[h], x1[h]);
+        bm = fmaxf(bm, __shfl_xor(bm, 8, 64));
+        bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+        bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+        if (bm > m[h] + kLazyRescale) {  // wave-uniform
+          const float alpha = m[h] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m[h] - bm);
+#pragma unroll
+          for (int cc = 0; cc < CPL; ++cc) acc[h][cc] *= alpha;
+#pragma unroll
+          for (int u = 0; u < PPL; ++u)
+            if ((cg + 8 * u) % G == h) lpart[u] *= alpha;
+          m[h] = bm;
+        }
+      }
+    }
+    // publish p for the (token, head) pairs this lane owns
+#pragma unroll
+    for (int u = 0; u < PPL; ++u) {
+      const int pr = cg + 8 * u;
+      if (pr < PAIRS) {
+        const int h = pr % G;
+        const bool second = pr >= G;
+        float x = x0[0];
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh)
+          if (hh == h) x = second ? x1[hh] : x0[hh];
+        float mh = m[0];
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh)
+          if (hh == h) mh = m[hh];
+        const float p = x == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(x - mh);
+        lpart[u] += p;
+        sm.p[wave][second ? tp + 8 : tp][h] = p;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    if (valid < kBlock) vr.mask_tokens(valid);  // slots past the sequence end may hold anything
+#pragma unroll
+    for (int t = 0; t < kBlock; ++t) {
+      float pt[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) pt[h] = sm.p[wave][t][h];
+#pragma unroll
+      for (int cc = 0; cc < CPL; ++cc) {
+        const float vv = vr.get(cc, t);
+#pragma unroll
+        for (int h = 0; h < G; ++h) acc[h][cc] = fmaf(pt[h], vv, acc[h][cc]);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (it + 1 < nw) {
+      k0 = nk0;
+      k1 = nk1;
+      vr = nvr;
+    }
+  }
+
+  // wave state -> LDS
+  float lsum[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) lsum[h] = 0.f;
+#pragma unroll
+  for (int u = 0; u < PPL; ++u) {
+    const int pr = cg + 8 * u;
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+      if (pr < PAIRS && pr % G == h) lsum[h] += lpart[u];
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) lsum[h] += __shfl_xor(lsum[h], o, 64);
+    if (lane == 0) {
+      sm.m[wave][h] = nw > 0 ? m[h] : -__builtin_inff();
+      sm.l[wave][h] = nw > 0 ? lsum[h] : 0.f;
+    }
+#pragma unroll
+    for (int cc = 0; cc < CPL; ++cc) sm.acc[wave][h][lane * CPL + cc] = acc[h][cc];
+  }
+  __syncthreads();
+  // merge the waves into this split's partial: thread -> (head, channels)
+  const size_t part = gi * a.splits + s;
+  for (int i = tid; i < G * D; i += kDecThreads) {
+    const int h = i / D, ch = i % D;
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) mx = fmaxf(mx, sm.m[w][h]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) {
+      const float mw = sm.m[w][h];
+      const float e = mw == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(mw - mx);
+      num = fmaf(e, sm.acc[w][h][ch], num);
+      den = fmaf(e, sm.l[w][h], den);
+    }
+    a.part_acc[(part * G + h) * D + ch] = num;
+    if (ch == 0) {
+      a.part_ml[(part * G + h) * 2 + 0] = mx;
+      a.part_ml[(part * G + h) * 2 + 1] = den;
+    }
+  }
+}
+
+// grid: x = KV head, y = sequence; 256 threads: merge a group's splits.
+template <typename T, int D, int G>
+__global__ __launch_bounds__(kDecThreads) void k_decode_combine(DecodeArgs a, void* __restrict__ out) {
+  const CacheView& c = a.c;
+  const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const size_t gi = size_t(b) * c.Hkv + g;
+  const int live = (a.count[b] + a.bps - 1) / a.bps;
+  for (int i = tid; i < G * D; i += kDecThreads) {
+    const int h = i / D, ch = i % D;
+    const float* ml = a.part_ml + (gi * a.splits * G + h) * 2;  // split sp at ml[sp * G * 2]
+    const float* acc = a.part_acc + (gi * a.splits * G + h) * D + ch;
+    float mx = -__builtin_inff();
+    for (int sp = 0; sp < live; ++sp) mx = fmaxf(mx, ml[sp * G * 2]);
+    float num = 0.f, den = 0.f;
+#pragma unroll 4
+    for (int sp = 0; sp < live; ++sp) {
+      const float ms = ml[sp * G * 2];
+      const float e = ms == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(ms - mx);
+      num = fmaf(e, acc[size_t(sp) * G * D], num);
+      den = fmaf(e, ml[sp * G * 2 + 1], den);
+    }
+    store_out<T>(out, (size_t(b) * c.Hq + size_t(g) * G + h) * D + ch, num / den);
+  }
 }
 
 template <typename T, int D, int G>
 hipError_t launch_decode_t(const DecodeArgs& a, void* out, hipStream_t st) {
   const CacheView& c = a.c;
-  dim3 g1(a.splits, c.Hkv, c.B);
-  hipLaunchKernelGGL((k_decode_split<T, D, G>), g1, dim3(64), 0, st, a);
+  dim3 grid(a.splits, c.Hkv, c.B);
+  hipLaunchKernelGGL((k_decode<T, D, G>), grid, dim3(kDecThreads), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 g2(c.Hq, c.B);
-  hipLaunchKernelGGL((k_decode_combine<T, D>), g2, dim3(64), 0, st, a.part_ml, a.part_acc, a.count, c.Hq,
-                     a.bps, a.splits, out);
+  dim3 g2(c.Hkv, c.B);
+  hipLaunchKernelGGL((k_decode_combine<T, D, G>), g2, dim3(kDecThreads), 0, st, a, out);
   return hipGetLastError();
 }
 
@@ -325,11 +432,11 @@ hipError_t launch_decode_g(const DecodeArgs& a, void* out, hipStream_t st) {
 }  // namespace
 
 DecodePlan plan_decode(const CacheView& c, int n_cap) {
-  // Aim for ~2048 single-wave workgroups (8 per CU) so the gathered loads of
-  // all CUs overlap; a split holds 4..64 blocks (one block id per lane).
+  // About 512 workgroups of 4 waves (2 per CU) over the largest selection; a
+  // split holds at most 256 blocks (64 per wave, one block id per lane).
   const long work = long(c.B) * c.Hkv * n_cap;
-  int bps = int((work + 2047) / 2048);
-  bps = bps < 4 ? 4 : (bps > 64 ? 64 : bps);
+  int bps = int((work + 511) / 512);
+  bps = bps < 4 ? 4 : (bps > 256 ? 256 : bps);
   DecodePlan p;
   p.bps = bps;
   p.splits = (n_cap + bps - 1) / bps;
@@ -338,14 +445,15 @@ DecodePlan plan_decode(const CacheView& c, int n_cap) {
 
 size_t decode_ws_bytes(const CacheView& c, int n_cap) {
   const DecodePlan p = plan_decode(c, n_cap);
-  const size_t slots = size_t(c.B) * c.Hq * p.splits;
-  return align_up(slots * 2 * sizeof(float), 256) + slots * c.D * sizeof(float);
+  const size_t parts = size_t(c.B) * c.Hkv * p.splits * c.G;
+  return align_up(parts * 2 * sizeof(float), 256) + parts * c.D * sizeof(float);
 }
 
 hipError_t launch_decode(const CacheView& c, const void* q, const int32_t* idx, const int32_t* count,
                          int n_cap, float scale, void* out, void* ws, hipStream_t st) {
   const DecodePlan p = plan_decode(c, n_cap);
-  const size_t slots = size_t(c.B) * c.Hq * p.splits;
+  const size_t parts = size_t(c.B) * c.Hkv * p.splits * c.G;
+  char* w = static_cast<char*>(ws);
   DecodeArgs a;
   a.c = c;
   a.q = q;
@@ -355,8 +463,8 @@ hipError_t launch_decode(const CacheView& c, const void* q, const int32_t* idx, 
   a.bps = p.bps;
   a.splits = p.splits;
   a.scale_log2 = scale * 1.4426950408889634f;
-  a.part_ml = static_cast<float*>(ws);
-  a.part_acc = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(slots * 2 * sizeof(float), 256));
+  a.part_ml = reinterpret_cast<float*>(w);
+  a.part_acc = reinterpret_cast<float*>(w + align_up(parts * 2 * sizeof(float), 256));
   if (c.dtype == RESA_BF16)
     return c.D == 128 ? launch_decode_g<uint16_t, 128>(a, out, st) : launch_decode_g<uint16_t, 64>(a, out, st);
   return c.D == 128 ? launch_decode_g<float, 128>(a, out, st) : launch_decode_g<float, 64>(a, out, st);

@@ -8,7 +8,8 @@
 // read by the 64 lanes in one coalesced access (lane owns head_dim/64 channels),
 // so a block costs 16 row reads of 128-512 bytes and one 2-row descriptor write.
 // The same kernel performs the append: tokens in the refreshed range come from
-// k_new/v_new, are stored into their page, and enter the min/max directly.
+// k_new/v_new, are stored into their page (K token-major, V channel-major), and
+// enter the min/max directly.
 #include "resa_internal.h"
 
 namespace resa {
@@ -53,23 +54,34 @@ __global__ __launch_bounds__(64) void k_refresh_blocks(CacheView c, const void* 
     mn[e] = __builtin_inff();
     mx[e] = -__builtin_inff();
   }
-  for (int t = 0; t < valid; ++t) {
-    const int pos = j * kBlock + t;
-    const bool fresh = n_new > 0 && pos >= lo && k_new != nullptr;
-    const size_t src_row = fresh ? (size_t(b) * n_new + (pos - (L - n_new))) * c.Hkv + g : 0;
+  // All 16 rows are read with unconditional loads (slots past the end re-read
+  // slot 0 and are ignored) so they are in flight together; fresh rows come
+  // from k_new and are stored into the page.
+  float kv[kBlock][CPL];
+#pragma unroll
+  for (int t = 0; t < kBlock; ++t)
+#pragma unroll
+    for (int e = 0; e < CPL; ++e)
+      kv[t][e] = Elem<T>::load(c.k, (row0 + (t < valid ? t : 0)) * D + lane + 64 * e);
+  const int first_new = n_new > 0 && k_new != nullptr ? lo - j * kBlock : kBlock;  // slot of the first fresh row
+#pragma unroll
+  for (int t = 0; t < kBlock; ++t) {
+    if (t >= valid) continue;
+    if (t >= first_new) {
+      const size_t src_row = (size_t(b) * n_new + (j * kBlock + t - (L - n_new))) * c.Hkv + g;
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) {
+        const int ch = lane + 64 * e;
+        kv[t][e] = Elem<T>::load(k_new, src_row * D + ch);
+        Elem<T>::store(c.kw, (row0 + t) * D + ch, kv[t][e]);
+        // V tiles are channel-major: [page][head][channel][slot]
+        Elem<T>::store(c.vw, (row0 * D + size_t(ch) * kBlock) + t, Elem<T>::load(v_new, src_row * D + ch));
+      }
+    }
 #pragma unroll
     for (int e = 0; e < CPL; ++e) {
-      const int ch = lane + 64 * e;
-      float x;
-      if (fresh) {
-        x = Elem<T>::load(k_new, src_row * D + ch);
-        Elem<T>::store(c.kw, (row0 + t) * D + ch, x);
-        Elem<T>::store(c.vw, (row0 + t) * D + ch, Elem<T>::load(v_new, src_row * D + ch));
-      } else {
-        x = Elem<T>::load(c.k, (row0 + t) * D + ch);
-      }
-      mn[e] = fminf(mn[e], x);
-      mx[e] = fmaxf(mx[e], x);
+      mn[e] = fminf(mn[e], kv[t][e]);
+      mx[e] = fmaxf(mx[e], kv[t][e]);
     }
   }
   const size_t d0 = (size_t(page) * c.Hkv + g) * 2 * D;

@@ -14,8 +14,8 @@
 // lane holds 16 keys of one query row: the softmax row max needs one cross-lane
 // step, and the probabilities feed the second product O^T = V^T P^T as its B
 // operand with no data movement (the key order inside a 16-key step is the same
-// permutation on both operands). V is stored transposed in LDS for the A
-// operand. Partial (m, l, O) per row and chunk go to the workspace; a combine
+// permutation on both operands). V pages are channel-major in HBM, so the V^T
+// tile for the A operand is copied into LDS with plain 16-byte stores. Partial (m, l, O) per row and chunk go to the workspace; a combine
 // kernel merges the chunks with log-sum-exp weights.
 //
 // fp32 path (k_rect_valu): one wave per (sequence, row, head), plain VALU.
@@ -91,24 +91,47 @@ __global__ __launch_bounds__(256) void k_rect_mfma(RectArgs a) {
 
   const uint16_t* kb = static_cast<const uint16_t*>(c.k);
   const uint16_t* vb = static_cast<const uint16_t*>(c.v);
-  const int lk = tid / 8;            // key of the tile this thread loads
-  const int lc = (tid % 8) * EPT;    // first column it loads
+  // K: thread -> (key lk, columns lc .. lc + EPT) of the token-major K rows.
+  // V: the page tiles are channel-major (d x 16 tokens); thread -> 16-byte
+  // pieces u = tid + 256 e: page pg of the tile, channel ch, 8 tokens at 8 vh.
+  const int lk = tid / 8;
+  const int lc = (tid % 8) * EPT;
   uint4 kreg[EPT / 8], vreg[EPT / 8];
-  // Keys past the chunk end are loaded from the chunk's first key (always valid)
-  // and then zeroed, so uninitialised slots never reach the products.
+  // Keys past the chunk end are read from the chunk's first key (always valid)
+  // and zeroed, so uninitialised slots never reach the products.
   auto load_tile = [&](int base) {
-    const int key = base + lk;
-    const bool ok = key < key_hi;
-    const int kk = ok ? key : key_lo;
-    const int page = c.bt[size_t(b) * c.maxb + (kk >> 4)];
-    const size_t off = ((size_t(page) * c.Hkv + g) * kBlock + (kk & 15)) * D + lc;
-    const uint32_t keep = ok ? 0xffffffffu : 0u;
+    {
+      const int key = base + lk;
+      const bool ok = key < key_hi;
+      const int kk = ok ? key : key_lo;
+      const int page = c.bt[size_t(b) * c.maxb + (kk >> 4)];
+      const size_t off = ((size_t(page) * c.Hkv + g) * kBlock + (kk & 15)) * D + lc;
+      const uint32_t keep = ok ? 0xffffffffu : 0u;
+#pragma unroll
+      for (int e = 0; e < EPT / 8; ++e) {
+        const uint4 kv = *reinterpret_cast<const uint4*>(kb + off + 8 * e);
+        kreg[e] = make_uint4(kv.x & keep, kv.y & keep, kv.z & keep, kv.w & keep);
+      }
+    }
 #pragma unroll
     for (int e = 0; e < EPT / 8; ++e) {
-      uint4 kv = *reinterpret_cast<const uint4*>(kb + off + 8 * e);
-      uint4 vv = *reinterpret_cast<const uint4*>(vb + off + 8 * e);
-      kreg[e] = make_uint4(kv.x & keep, kv.y & keep, kv.z & keep, kv.w & keep);
-      vreg[e] = make_uint4(vv.x & keep, vv.y & keep, vv.z & keep, vv.w & keep);
+      const int u = tid + 256 * e;
+      const int pg = u / (2 * D), ch = (u % (2 * D)) / 2, vh = u % 2;
+      const int t0 = base + pg * 16 + vh * 8;  // key of the first of the 8 tokens
+      const int kk = t0 < key_hi ? t0 : key_lo;
+      const int page = c.bt[size_t(b) * c.maxb + (kk >> 4)];
+      const size_t off = ((size_t(page) * c.Hkv + g) * D + ch) * kBlock + (t0 < key_hi ? vh * 8 : 0);
+      uint4 vv = *reinterpret_cast<const uint4*>(vb + off);
+      const int nvalid = key_hi - t0;  // tokens of the 8 that exist
+      if (nvalid < 8) {
+        const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+          o[x] = w[x] & ((2 * x < nvalid ? 0x0000ffffu : 0u) | (2 * x + 1 < nvalid ? 0xffff0000u : 0u));
+        vv = make_uint4(o[0], o[1], o[2], o[3]);
+      }
+      vreg[e] = vv;
     }
   };
 
@@ -118,12 +141,9 @@ __global__ __launch_bounds__(256) void k_rect_mfma(RectArgs a) {
 #pragma unroll
     for (int e = 0; e < EPT / 8; ++e) {
       *reinterpret_cast<uint4*>(&sm.k[lk * RectSmem<D>::KS + lc + 8 * e]) = kreg[e];
-      const uint32_t w[4] = {vreg[e].x, vreg[e].y, vreg[e].z, vreg[e].w};
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        sm.vt[(lc + 8 * e + 2 * x) * RectSmem<D>::VS + lk] = uint16_t(w[x] & 0xffffu);
-        sm.vt[(lc + 8 * e + 2 * x + 1) * RectSmem<D>::VS + lk] = uint16_t(w[x] >> 16);
-      }
+      const int u = tid + 256 * e;
+      const int pg = u / (2 * D), ch = (u % (2 * D)) / 2, vh = u % 2;
+      *reinterpret_cast<uint4*>(&sm.vt[ch * RectSmem<D>::VS + pg * 16 + vh * 8]) = vreg[e];
     }
     __syncthreads();
     if (base + kRectTileKeys < key_hi) load_tile(base + kRectTileKeys);
@@ -299,9 +319,10 @@ __global__ __launch_bounds__(64) void k_rect_valu(RectArgs a, void* __restrict__
     for (int k = 0; k < nt; ++k) {
       const int tt = t0 + k;
       const int page = c.bt[size_t(b) * c.maxb + (tt >> 4)];
-      const size_t row = ((size_t(page) * c.Hkv + g) * kBlock + (tt & 15)) * D;
+      const size_t vt = (size_t(page) * c.Hkv + g) * D * kBlock + (tt & 15);  // channel-major V tile
 #pragma unroll
-      for (int e = 0; e < D / 64; ++e) acc[e] = fmaf(ps[k], load_elem<T>(c.v, row + lane + 64 * e), acc[e]);
+      for (int e = 0; e < D / 64; ++e)
+        acc[e] = fmaf(ps[k], load_elem<T>(c.v, vt + size_t(lane + 64 * e) * kBlock), acc[e]);
     }
   }
   const size_t oo = ((size_t(b) * a.f + i) * c.Hq + h) * D;
@@ -361,8 +382,9 @@ hipError_t launch_rectify_attention(const CacheView& c, const void* q, int f, fl
   a.splits = p.splits;
   a.scale_log2 = scale * 1.4426950408889634f;
   const size_t slots = size_t(c.B) * c.Hkv * p.splits * p.rows_pad;
-  a.part_ml = static_cast<float*>(ws);
-  a.part_acc = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(slots * 2 * sizeof(float), 256));
+  char* scratch = static_cast<char*>(ws);
+  a.part_ml = reinterpret_cast<float*>(scratch);
+  a.part_acc = reinterpret_cast<float*>(scratch + align_up(slots * 2 * sizeof(float), 256));
   if (c.dtype == RESA_BF16) return c.D == 128 ? launch_mfma<128>(a, out, st) : launch_mfma<64>(a, out, st);
   dim3 grid(c.Hq, f, c.B);
   if (c.D == 128)

@@ -2,51 +2,68 @@
 // carries the argument"; count rule Eq. 5 from its referee report, major
 // comment 1, with an explicit active ratio r).
 //
-// k_score: every KV-head group pools its G query heads into their mean q_bar
-// (float64, summed in head order), then scores every block with the Quest upper
-// bound sum_c max(q_bar_c kmin_c, q_bar_c kmax_c). Kernel form: per channel the
-// product with the larger value is q_bar_c * (q_bar_c >= 0 ? kmax_c : kmin_c);
-// the two agree exactly because kmin <= kmax and rounding is monotone (and the
-// float64 products of bf16 / fp32 keys with q_bar are exact). One wave scores one
-// page for all KV heads: a page's descriptors for all heads are one contiguous
-// [Hkv][2][D] record, read with 16-byte lane loads. Scores go to the workspace.
+// k_score, grid (block chunk, KV head, sequence): every workgroup scores
+// kScoreChunk blocks of one (sequence, KV head) group. The group's G query
+// heads are pooled into their mean q_bar (float64, summed in head order), and
+// block j gets the Quest upper bound
+//   s_j = sum_c max(q_bar_c kmin_jc, q_bar_c kmax_jc),
+// evaluated as q_bar_c * (q_bar_c >= 0 ? kmax_jc : kmin_jc): the two are equal
+// because kmin <= kmax, rounding is monotone and these float64 products of
+// bf16/fp32 keys are exact. A block's descriptor record for one head is
+// 2 x head_dim contiguous elements; head_dim/8 lanes read it with 16-byte loads
+// (all of a lane's loads are issued before any is used), and the lanes' float64
+// partials are summed with DPP moves inside a row. Scores go to the workspace.
 //
-// k_topn: one workgroup per (sequence, KV head). n = min(M, max(n_min,
+// k_topn, grid (KV head, sequence), 1024 threads: n = min(M, max(n_min,
 // ceil(M r))) in IEEE double; the min(n_local, n) newest blocks are always
 // taken; the other places go to the highest scores, ties to the lower index.
-// The threshold is found exactly by an 8-pass radix select (8-bit digits) on
-// order-preserving 64-bit keys of the float64 scores, held in registers; then
-// two workgroup scans place equal-key ties in index order and write the chosen
-// indices in ascending order.
+// The candidates' order-preserving 64-bit keys stay in registers. The
+// threshold is found exactly by radix selection with 8-bit digits starting
+// below the common prefix of the candidates' key range (per-wave LDS
+// histograms keep atomic contention inside a wave) until the candidates that
+// share the threshold's prefix number at most 64; one wave then ranks those
+// exactly (key descending, index ascending). Chosen blocks are marked in an LDS
+// bitmap and compacted in index order, so the output is sorted ascending.
+//
+// The two kernels hand over through the workspace at the kernel boundary: a
+// cross-workgroup hand-off inside one kernel would need device-scope fences,
+// which write back and invalidate a whole L2 on this multi-die part.
 #include "resa_internal.h"
 
 namespace resa {
 namespace {
 
-constexpr int kScoreBlocksPerWave = 16;
-constexpr int kScoreWaves = 4;
-constexpr int kScoreBlocksPerWg = kScoreBlocksPerWave * kScoreWaves;
-constexpr int kMaxQbar = 4096;  // Hkv * D doubles in LDS (32 KiB)
+constexpr int kScoreThreads = 256;
+constexpr int kScoreChunk = 64;  // blocks scored per workgroup
+constexpr int kTopnWaves = kTopnThreads / 64;
+constexpr int kBitmapWords = kTopnThreads * kTopnMaxPerThread / 32;  // 1024
+constexpr int kRankGroup = 64;
 
 template <typename T>
-struct Chunk8;  // 8 consecutive channels of a descriptor row, widened exactly
+struct Chunk8;  // 8 consecutive channels of a descriptor row
 template <>
 struct Chunk8<uint16_t> {
-  __device__ static void load(const void* base, size_t off, float (&x)[8]) {
-    const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
-    x[0] = bf16_lo(u.x); x[1] = bf16_hi(u.x);
-    x[2] = bf16_lo(u.y); x[3] = bf16_hi(u.y);
-    x[4] = bf16_lo(u.z); x[5] = bf16_hi(u.z);
-    x[6] = bf16_lo(u.w); x[7] = bf16_hi(u.w);
+  uint4 u;
+  __device__ void load(const void* base, size_t off) {
+    u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
+  }
+  __device__ float get(int e) const {
+    const uint32_t w = e < 2 ? u.x : e < 4 ? u.y : e < 6 ? u.z : u.w;
+    return (e & 1) ? bf16_hi(w) : bf16_lo(w);
   }
 };
 template <>
 struct Chunk8<float> {
-  __device__ static void load(const void* base, size_t off, float (&x)[8]) {
+  float4 a, b;
+  __device__ void load(const void* base, size_t off) {
     const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
-    const float4 a = p[0], b = p[1];
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    a = p[0];
+    b = p[1];
+  }
+  __device__ float get(int e) const {
+    const float4 w = e < 4 ? a : b;
+    const int r = e & 3;
+    return r == 0 ? w.x : r == 1 ? w.y : r == 2 ? w.z : w.w;
   }
 };
 
@@ -56,56 +73,76 @@ __device__ __forceinline__ float load_q(const void* q, size_t i) {
   else return static_cast<const float*>(q)[i];
 }
 
-// grid: x = chunk of kScoreBlocksPerWg blocks, y = sequence.
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const uint64_t u = uint64_t(__double_as_longlong(x));
+  const int lo = __builtin_amdgcn_mov_dpp(int(uint32_t(u)), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_mov_dpp(int(uint32_t(u >> 32)), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double((long long)((uint64_t(uint32_t(hi)) << 32) | uint32_t(lo)));
+}
+
+// Sum over aligned groups of N lanes (N = 8 or 16, inside one DPP row). Lane 0
+// of each group always adds in the same order, so its result is deterministic.
+template <int N>
+__device__ __forceinline__ double row_sum_f64(double x) {
+  if constexpr (N == 16) x += dpp_f64<0x128>(x);  // row_ror:8 pairs lanes i and i^8
+  x += dpp_f64<kDppHalfMirror>(x);                 // then an 8-lane butterfly
+  x += dpp_f64<kDppQuadXor1>(x);
+  x += dpp_f64<kDppQuadXor2>(x);
+  return x;
+}
+
+// grid: x = chunk of kScoreChunk blocks, y = KV head, z = sequence.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void k_score(CacheView c, const void* __restrict__ q,
-                                               double* __restrict__ scores) {
-  constexpr int LPH = D / 8;       // lanes per head (8 channels each)
-  constexpr int HPP = 64 / LPH;    // heads per pass
-  __shared__ double qbar[kMaxQbar];
-  const int b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__global__ __launch_bounds__(kScoreThreads) void k_score(CacheView c, const void* __restrict__ q,
+                                                         double* __restrict__ scores) {
+  constexpr int LPB = D / 8;     // lanes per block record (8 channels each)
+  constexpr int BPW = 64 / LPB;  // blocks per wave per row of loads
+  constexpr int ROWS = kScoreChunk / (4 * BPW);
+  const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int L = c.seq_lens[b];
   const int M = (L + kBlock - 1) / kBlock;
-  const int j0 = blockIdx.x * kScoreBlocksPerWg;
-  if (j0 >= M) return;
+  if (chunk * kScoreChunk >= M) return;
+  const size_t gi = size_t(b) * c.Hkv + g;
+  const int sub = lane % LPB, slot = lane / LPB, c0 = sub * 8;
 
-  for (int i = tid; i < c.Hkv * D; i += 256) {
-    const int g = i / D, ch = i % D;
-    const size_t base = (size_t(b) * c.Hq + size_t(g) * c.G) * D + ch;
-    double acc = double(load_q<T>(q, base));
-    for (int h = 1; h < c.G; ++h) acc += double(load_q<T>(q, base + size_t(h) * D));
-    qbar[i] = acc / double(c.G);
+  // All page ids, then all descriptor loads, are issued unconditionally (blocks
+  // past the sequence end re-read block 0) so they are in flight together.
+  int jr[ROWS], page[ROWS];
+  Chunk8<T> lo[ROWS], hi[ROWS];
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) {
+    jr[r] = chunk * kScoreChunk + (r * 4 + wave) * BPW + slot;
+    page[r] = c.bt[size_t(b) * c.maxb + (jr[r] < M ? jr[r] : 0)];
   }
-  __syncthreads();
-
-  const int jw = j0 + wave * kScoreBlocksPerWave;
-  // page ids of this wave's blocks, one per lane, read back with readlane
-  int my_page = 0;
-  if (lane < kScoreBlocksPerWave && jw + lane < M) my_page = c.bt[size_t(b) * c.maxb + jw + lane];
-  const int nblk = min(kScoreBlocksPerWave, M - jw);
-  const int passes = (c.Hkv + HPP - 1) / HPP;
-  const int sub = lane % LPH, c0 = sub * 8;
-  for (int jj = 0; jj < nblk; ++jj) {
-    const int page = __builtin_amdgcn_readlane(my_page, jj);
-    for (int p = 0; p < passes; ++p) {
-      const int g = p * HPP + lane / LPH;
-      double part = 0.0;
-      if (g < c.Hkv) {
-        const size_t rec = (size_t(page) * c.Hkv + g) * 2 * D;
-        float kmin[8], kmax[8];
-        Chunk8<T>::load(c.desc, rec + c0, kmin);
-        Chunk8<T>::load(c.desc, rec + D + c0, kmax);
-        const double* qb = qbar + g * D + c0;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const double qv = qb[e];
-          part += qv * double(qv >= 0.0 ? kmax[e] : kmin[e]);
-        }
-      }
+  for (int r = 0; r < ROWS; ++r) {
+    const size_t rec = (size_t(page[r]) * c.Hkv + g) * 2 * D;
+    lo[r].load(c.desc, rec + c0);
+    hi[r].load(c.desc, rec + D + c0);
+  }
+  // pooled query for this lane's 8 channels (overlaps the descriptor loads)
+  double qb[8];
+  {
+    const size_t base = (size_t(b) * c.Hq + size_t(g) * c.G) * D + c0;
 #pragma unroll
-      for (int m = 1; m < LPH; m <<= 1) part += shfl_xor_f64(part, m);
-      if (g < c.Hkv && sub == 0) scores[(size_t(b) * c.Hkv + g) * c.maxb + jw + jj] = part;
+    for (int e = 0; e < 8; ++e) qb[e] = double(load_q<T>(q, base + e));
+    for (int h = 1; h < c.G; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qb[e] += double(load_q<T>(q, base + size_t(h) * D + e));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qb[e] = qb[e] / double(c.G);
+  }
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) {
+    double part = 0.0;
+    if (jr[r] < M) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part += qb[e] * double(qb[e] >= 0.0 ? hi[r].get(e) : lo[r].get(e));
     }
+    part = row_sum_f64<LPB>(part);
+    if (sub == 0 && jr[r] < M) scores[gi * c.maxb + jr[r]] = part;
   }
 }
 
@@ -115,166 +152,266 @@ __device__ __forceinline__ uint64_t order_key(double s) {
   return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
 
-// Exclusive scan of one int per thread over a 1024-thread workgroup.
-__device__ int wg_exclusive_scan(int v, int* wave_tot, int& total) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+struct TopnSmem {
+  int hist[kTopnWaves][256];
+  int tot[256];
+  uint32_t sel[kBitmapWords];
+  uint32_t tie[kBitmapWords];
+  uint64_t red_max[kTopnWaves], red_min[kTopnWaves];
+  int scan[kTopnWaves];
+  uint64_t gk[kRankGroup];
+  int gj[kRankGroup];
+  int gcount;
+  int digit, k_rem, gsize;
+};
+
+// Exclusive scan over the 1024 threads; `total` gets the sum.
+__device__ __forceinline__ int wg_exclusive_scan(int v, int* tmp, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int x = v;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const int y = __shfl_up(x, o, 64);
     if (lane >= o) x += y;
   }
-  if (lane == 63) wave_tot[wave] = x;
+  if (lane == 63) tmp[wave] = x;
   __syncthreads();
-  if (wave == 0) {
-    int t = lane < kTopnThreads / 64 ? wave_tot[lane] : 0;
+  int before = 0;
+  total = 0;
 #pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      const int y = __shfl_up(t, o, 64);
-      if (lane >= o) t += y;
-    }
-    if (lane < kTopnThreads / 64) wave_tot[16 + lane] = t;  // inclusive wave prefix
+  for (int w = 0; w < kTopnWaves; ++w) {
+    const int t = tmp[w];
+    before += w < wave ? t : 0;
+    total += t;
   }
-  __syncthreads();
-  const int before = wave == 0 ? 0 : wave_tot[16 + wave - 1];
-  total = wave_tot[16 + kTopnThreads / 64 - 1];
   __syncthreads();
   return before + x - v;
 }
 
-// grid: x = KV head, y = sequence.
+// grid: x = KV head, y = sequence; 1024 threads.
 __global__ __launch_bounds__(kTopnThreads) void k_topn(const double* __restrict__ scores,
                                                        const int32_t* __restrict__ seq_lens, int maxb,
-                                                       int Hkv, resa_select_params p,
-                                                       int32_t* __restrict__ idx,
+                                                       int Hkv, resa_select_params p, int32_t* __restrict__ idx,
                                                        int32_t* __restrict__ count, int n_cap) {
-  __shared__ int hist[256];
-  __shared__ int wave_tot[32];
-  __shared__ int found_digit, found_k;
+  __shared__ TopnSmem sm;
   const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int L = seq_lens[b];
   const int M = (L + kBlock - 1) / kBlock;
   const int n = min(M, max(p.n_min, int(ceil(double(M) * p.r))));
   if (g == 0 && tid == 0) count[b] = n;
-  const int keep_local = min(p.n_local, n);
-  const int quota = n - keep_local;
-  const int Mo = M - keep_local;  // candidates are blocks 0 .. Mo-1
+  const int keep = min(p.n_local, n);
+  const int quota = n - keep;
+  const int Mo = M - keep;  // candidates: blocks 0 .. Mo-1
   const int E = (M + kTopnThreads - 1) / kTopnThreads;
-  const int j0 = tid * E;
-  const double* row = scores + (size_t(b) * Hkv + g) * maxb;
+  const size_t gi = size_t(b) * Hkv + g;
+  const double* row = scores + gi * maxb;
 
+  // keys of the candidates, block j = e * 1024 + tid. Every load is issued
+  // unconditionally (out-of-range ones re-read block 0, always in the
+  // workspace) so that all of them are in flight at once.
   uint64_t key[kTopnMaxPerThread];
+  uint64_t kmax = 0, kmin = ~0ull;
+  double sc[kTopnMaxPerThread];
 #pragma unroll
   for (int e = 0; e < kTopnMaxPerThread; ++e) {
-    const int j = j0 + e;
-    key[e] = (e < E && j < Mo) ? order_key(row[j]) : 0;
+    const int j = e * kTopnThreads + tid;
+    sc[e] = row[(e < E && j < Mo) ? j : 0];
+  }
+#pragma unroll
+  for (int e = 0; e < kTopnMaxPerThread; ++e) {
+    const int j = e * kTopnThreads + tid;
+    key[e] = (e < E && j < Mo) ? order_key(sc[e]) : 0;
+  }
+#pragma unroll
+  for (int e = 0; e < kTopnMaxPerThread; ++e) {
+    const int j = e * kTopnThreads + tid;
+    if (e < E && j < Mo) {
+      kmax = key[e] > kmax ? key[e] : kmax;
+      kmin = key[e] < kmin ? key[e] : kmin;
+    }
+  }
+  for (int i = tid; i < kBitmapWords; i += kTopnThreads) {
+    sm.sel[i] = 0;
+    sm.tie[i] = 0;
   }
 
-  uint64_t prefix = 0;
+  // mode: 0 none of the candidates, 1 every member of the prefix group,
+  // 2 the lowest indices of the (exactly tied) prefix group, 3 ranked group
+  int mode = 0;
+  uint64_t prefix = 0, mask = 0;
   int k = quota;
   if (quota > 0) {
-    for (int pass = 0; pass < 8; ++pass) {
-      const int shift = 56 - 8 * pass;
-      const uint64_t hi_mask = pass == 0 ? 0 : (~0ull << (shift + 8));
-      for (int i = tid; i < 256; i += kTopnThreads) hist[i] = 0;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const uint64_t x = __shfl_xor(kmax, o, 64), y = __shfl_xor(kmin, o, 64);
+      kmax = x > kmax ? x : kmax;
+      kmin = y < kmin ? y : kmin;
+    }
+    if (lane == 0) {
+      sm.red_max[wave] = kmax;
+      sm.red_min[wave] = kmin;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kTopnWaves; ++w) {
+      kmax = sm.red_max[w] > kmax ? sm.red_max[w] : kmax;
+      kmin = sm.red_min[w] < kmin ? sm.red_min[w] : kmin;
+    }
+    const int plen = kmax == kmin ? 64 : __clzll((long long)(kmax ^ kmin));
+    mask = plen == 0 ? 0ull : (~0ull << (64 - plen));
+    prefix = kmax & mask;
+    int gsize = Mo;  // every candidate lies in [kmin, kmax], so shares the prefix
+    int bits_left = 64 - plen;
+    while (gsize > kRankGroup && gsize != k && bits_left > 0) {
+      const int nb = bits_left < 8 ? bits_left : 8;
+      const int shift = bits_left - nb;
+      const int nbins = 1 << nb;
+      for (int i = tid; i < kTopnWaves * 256; i += kTopnThreads) (&sm.hist[0][0])[i] = 0;
       __syncthreads();
 #pragma unroll
       for (int e = 0; e < kTopnMaxPerThread; ++e) {
-        const int j = j0 + e;
-        if (e < E && j < Mo && (key[e] & hi_mask) == prefix)
-          atomicAdd(&hist[int(key[e] >> shift) & 255], 1);
+        const int j = e * kTopnThreads + tid;
+        if (e < E && j < Mo && (key[e] & mask) == prefix)
+          atomicAdd(&sm.hist[wave][int(key[e] >> shift) & (nbins - 1)], 1);
+      }
+      __syncthreads();
+      if (tid < 256) {
+        int t = 0;
+#pragma unroll
+        for (int w = 0; w < kTopnWaves; ++w) t += sm.hist[w][tid];
+        sm.tot[tid] = t;
       }
       __syncthreads();
       if (tid < 64) {
-        // lane owns digits 4*lane .. 4*lane+3; count of larger digits via a
-        // suffix scan over lanes
+        // lane owns digits 4 lane .. 4 lane + 3; elements with larger digits
+        // come from a suffix sum over the lanes above
         const int d0 = 4 * tid;
-        const int h0 = hist[d0], h1 = hist[d0 + 1], h2 = hist[d0 + 2], h3 = hist[d0 + 3];
-        const int mine = h0 + h1 + h2 + h3;
+        const int h[4] = {sm.tot[d0], sm.tot[d0 + 1], sm.tot[d0 + 2], sm.tot[d0 + 3]};
+        const int mine = h[0] + h[1] + h[2] + h[3];
         int suf = mine;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
           const int y = __shfl_down(suf, o, 64);
           if (tid + o < 64) suf += y;
         }
-        int above = suf - mine;  // elements with a digit > 4*lane+3
-        const int hs[4] = {h0, h1, h2, h3};
+        int above = suf - mine;
 #pragma unroll
-        for (int q = 3; q >= 0; --q) {
-          if (above < k && above + hs[q] >= k) {
-            found_digit = d0 + q;
-            found_k = k - above;
+        for (int u = 3; u >= 0; --u) {
+          if (above < k && above + h[u] >= k) {
+            sm.digit = d0 + u;
+            sm.k_rem = k - above;
+            sm.gsize = h[u];
           }
-          above += hs[q];
+          above += h[u];
         }
       }
       __syncthreads();
-      prefix |= uint64_t(found_digit) << shift;
-      k = found_k;
-      __syncthreads();
+      prefix |= uint64_t(sm.digit) << shift;
+      mask |= uint64_t(nbins - 1) << shift;
+      k = sm.k_rem;
+      gsize = sm.gsize;
+      bits_left -= nb;
     }
-  }
-  const uint64_t T = prefix;  // key of the quota-th best candidate
-  const int take_eq = quota > 0 ? k : 0;
-
-  // rank equal keys by index
-  int n_eq = 0;
+    mode = gsize == k ? 1 : (bits_left == 0 ? 2 : 3);
+    if (mode == 3) {
+      if (tid == 0) sm.gcount = 0;
+      __syncthreads();
 #pragma unroll
-  for (int e = 0; e < kTopnMaxPerThread; ++e) {
-    const int j = j0 + e;
-    if (quota > 0 && e < E && j < Mo && key[e] == T) ++n_eq;
-  }
-  int tot;
-  int eq_rank = wg_exclusive_scan(n_eq, wave_tot, tot);
-  unsigned sel_bits = 0;
-  int n_sel = 0;
-#pragma unroll
-  for (int e = 0; e < kTopnMaxPerThread; ++e) {
-    const int j = j0 + e;
-    bool s = false;
-    if (e < E && j < M) {
-      if (j >= Mo) {
-        s = true;
-      } else if (quota > 0) {
-        if (key[e] > T) s = true;
-        else if (key[e] == T) s = (eq_rank++ < take_eq);
+      for (int e = 0; e < kTopnMaxPerThread; ++e) {
+        const int j = e * kTopnThreads + tid;
+        if (e < E && j < Mo && (key[e] & mask) == prefix) {
+          const int s = atomicAdd(&sm.gcount, 1);
+          sm.gk[s] = key[e];
+          sm.gj[s] = j;
+        }
+      }
+      __syncthreads();
+      if (tid < 64) {
+        const int gs = sm.gcount;
+        if (tid < gs) {
+          const uint64_t kt = sm.gk[tid];
+          const int jt = sm.gj[tid];
+          int rank = 0;
+          for (int u = 0; u < gs; ++u) {
+            const uint64_t ku = sm.gk[u];
+            rank += (ku > kt || (ku == kt && sm.gj[u] < jt)) ? 1 : 0;
+          }
+          if (rank < k) atomicOr(&sm.sel[jt >> 5], 1u << (jt & 31));
+        }
       }
     }
-    if (s) {
-      sel_bits |= 1u << e;
-      ++n_sel;
+  }
+  __syncthreads();
+  // mark the chosen blocks
+#pragma unroll
+  for (int e = 0; e < kTopnMaxPerThread; ++e) {
+    const int j = e * kTopnThreads + tid;
+    if (e >= E || j >= M) continue;
+    bool s = false, t = false;
+    if (j >= Mo) {
+      s = true;
+    } else if (mode != 0) {
+      const uint64_t km = key[e] & mask;
+      if (km > prefix) s = true;
+      else if (km == prefix) {
+        if (mode == 1) s = true;
+        else if (mode == 2) t = true;
+      }
+    }
+    if (s) atomicOr(&sm.sel[j >> 5], 1u << (j & 31));
+    if (t) atomicOr(&sm.tie[j >> 5], 1u << (j & 31));
+  }
+  __syncthreads();
+  // exactly tied threshold group: the k lowest indices
+  const int W = (M + 31) / 32;
+  uint32_t word = tid < W ? sm.sel[tid] : 0u;
+  if (mode == 2) {
+    const uint32_t tw = tid < W ? sm.tie[tid] : 0u;
+    int total;
+    int before = wg_exclusive_scan(__builtin_popcount(tw), sm.scan, total);
+    uint32_t f = tw;
+    while (f) {
+      const uint32_t bit = f & (~f + 1u);
+      if (before++ < k) word |= bit;
+      f &= f - 1u;
     }
   }
-  int pos = wg_exclusive_scan(n_sel, wave_tot, tot);
-  int32_t* out = idx + (size_t(b) * Hkv + g) * n_cap;
-#pragma unroll
-  for (int e = 0; e < kTopnMaxPerThread; ++e)
-    if (sel_bits & (1u << e)) out[pos++] = j0 + e;
+  int total;
+  int pos = wg_exclusive_scan(__builtin_popcount(word), sm.scan, total);
+  int32_t* out = idx + gi * n_cap;
+  while (word) {
+    const int e = __builtin_ctz(word);
+    word &= word - 1u;
+    out[pos++] = tid * 32 + e;
+  }
 }
 
 template <typename T, int D>
 hipError_t launch_select_t(const CacheView& c, const void* q, const resa_select_params& p, int32_t* idx,
-                           int32_t* count, int n_cap, void* ws, hipStream_t s) {
-  double* scores = static_cast<double*>(ws);
-  dim3 g1((c.maxb + kScoreBlocksPerWg - 1) / kScoreBlocksPerWg, c.B);
-  hipLaunchKernelGGL((k_score<T, D>), g1, dim3(256), 0, s, c, q, scores);
+                           int32_t* count, int n_cap, double* scores, hipStream_t s) {
+  dim3 g1((c.maxb + kScoreChunk - 1) / kScoreChunk, c.Hkv, c.B);
+  hipLaunchKernelGGL((k_score<T, D>), g1, dim3(kScoreThreads), 0, s, c, q, scores);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 g2(c.Hkv, c.B);
-  hipLaunchKernelGGL(k_topn, g2, dim3(kTopnThreads), 0, s, scores, c.seq_lens, c.maxb, c.Hkv, p, idx,
-                     count, n_cap);
+  hipLaunchKernelGGL(k_topn, g2, dim3(kTopnThreads), 0, s, scores, c.seq_lens, c.maxb, c.Hkv, p, idx, count,
+                     n_cap);
   return hipGetLastError();
 }
 
 }  // namespace
 
+size_t select_ws_bytes(const CacheView& c) { return size_t(c.B) * c.Hkv * c.maxb * sizeof(double); }
+
 hipError_t launch_select(const CacheView& c, const void* q, const resa_select_params& p, int32_t* idx,
                          int32_t* count, int n_cap, void* ws, hipStream_t s) {
+  double* scores = static_cast<double*>(ws);
   if (c.dtype == RESA_BF16)
-    return c.D == 128 ? launch_select_t<uint16_t, 128>(c, q, p, idx, count, n_cap, ws, s)
-                      : launch_select_t<uint16_t, 64>(c, q, p, idx, count, n_cap, ws, s);
-  return c.D == 128 ? launch_select_t<float, 128>(c, q, p, idx, count, n_cap, ws, s)
-                    : launch_select_t<float, 64>(c, q, p, idx, count, n_cap, ws, s);
+    return c.D == 128 ? launch_select_t<uint16_t, 128>(c, q, p, idx, count, n_cap, scores, s)
+                      : launch_select_t<uint16_t, 64>(c, q, p, idx, count, n_cap, scores, s);
+  return c.D == 128 ? launch_select_t<float, 128>(c, q, p, idx, count, n_cap, scores, s)
+                    : launch_select_t<float, 64>(c, q, p, idx, count, n_cap, scores, s);
 }
 
 }  // namespace resa

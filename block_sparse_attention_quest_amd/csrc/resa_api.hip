@@ -94,7 +94,7 @@ int32_t resa_n_cap(const resa_cache* cache, const resa_select_params* params) {
 size_t resa_select_workspace_size(const resa_cache* cache) {
   resa::CacheView v;
   if (check_cache(cache, &v) != RESA_OK) return 0;
-  return size_t(v.B) * v.Hkv * v.maxb * sizeof(double);
+  return resa::select_ws_bytes(v);
 }
 
 size_t resa_decode_workspace_size(const resa_cache* cache, int32_t n_cap) {
@@ -133,7 +133,7 @@ resa_status resa_select_blocks(const resa_cache* cache, const void* q, const res
   if (!q || !idx || !count) return fail(RESA_ERR_INVALID, "q, idx and count must not be NULL");
   const int need_cap = n_for((v.max_seq_len + resa::kBlock - 1) / resa::kBlock, params);
   if (n_cap < need_cap) return fail(RESA_ERR_INVALID, "n_cap %d is below resa_n_cap() = %d", n_cap, need_cap);
-  const size_t need = size_t(v.B) * v.Hkv * v.maxb * sizeof(double);
+  const size_t need = resa::select_ws_bytes(v);
   if (!ws || ws_bytes < need) return fail(RESA_ERR_WORKSPACE, "select workspace %zu < %zu bytes", ws_bytes, need);
   return hip_status(resa::launch_select(v, q, *params, idx, count, n_cap, ws, static_cast<hipStream_t>(stream)),
                     "resa_select_blocks");

@@ -76,6 +76,7 @@ hipError_t launch_update_tail(const CacheView& c, const void* k_new, const void*
                               hipStream_t s);
 hipError_t launch_rebuild(const CacheView& c, hipStream_t s);
 
+size_t select_ws_bytes(const CacheView& c);
 hipError_t launch_select(const CacheView& c, const void* q, const resa_select_params& p, int32_t* idx,
                          int32_t* count, int n_cap, void* ws, hipStream_t s);
 

@@ -100,7 +100,8 @@ class PagedKVCache:
                  device="cuda"):
         self.dtype = dtype
         self.k_pages = torch.zeros(num_pages, num_kv_heads, 16, head_dim, dtype=dtype, device=device)
-        self.v_pages = torch.zeros_like(self.k_pages)
+        # V pages are channel-major inside a page: [page][head][channel][slot]
+        self.v_pages = torch.zeros(num_pages, num_kv_heads, head_dim, 16, dtype=dtype, device=device)
         self.desc = torch.zeros(num_pages, num_kv_heads, 2, head_dim, dtype=dtype, device=device)
         self.block_table = torch.zeros(batch, max_blocks_per_seq, dtype=torch.int32, device=device)
         self.seq_lens = torch.zeros(batch, dtype=torch.int32, device=device)
@@ -176,4 +177,5 @@ def resa_rectify(cache: PagedKVCache, q: torch.Tensor, k_new: torch.Tensor, v_ne
 
 
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """A workspace for the calls (contents on entry do not matter)."""
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)

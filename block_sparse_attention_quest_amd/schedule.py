@@ -81,7 +81,8 @@ class ResaRunner:
                     k = torch.cat([k, torch.zeros(pad, w.head_dim, dtype=k.dtype)])
                     v = torch.cat([v, torch.zeros(pad, w.head_dim, dtype=v.dtype)])
                 c.k_pages[pages, h] = k.view(M, 16, w.head_dim).to(self.device)
-                c.v_pages[pages, h] = v.view(M, 16, w.head_dim).to(self.device)
+                # V tiles are stored channel-major: [page][head][channel][slot]
+                c.v_pages[pages, h] = v.view(M, 16, w.head_dim).transpose(1, 2).contiguous().to(self.device)
 
     # -- the hot path -------------------------------------------------------
     def build_descriptors(self) -> None:

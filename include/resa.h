@@ -19,8 +19,14 @@
  *    returns RESA_ERR_INVALID or RESA_ERR_UNSUPPORTED and launches nothing; a
  *    failed launch returns RESA_ERR_HIP. resa_last_error() then gives a message.
  *  - Device-side preconditions (seq_lens[b] <= max_seq_len, block_table entries
- *    in [0, num_pages) for every block a sequence holds, f <= seq_lens[b]) are the
+ *    in [0, num_pages) for every block a sequence holds, seq_lens[b] >= 1 for
+ *    selection and decoding, f <= seq_lens[b] for rectification) are the
  *    caller's; they are not checked.
+ *  - Workspaces: each call takes a caller-owned workspace of at least the size
+ *    its *_workspace_size() function returns. Its contents on entry do not
+ *    matter and are dead on return, so one workspace may serve all calls issued
+ *    in order on one stream. Calls that may run concurrently need separate
+ *    workspaces.
  *  - The library holds no mutable state apart from the thread-local error text,
  *    so calls on different streams from different host threads are safe as long
  *    as they do not share output buffers or workspace.
@@ -50,7 +56,9 @@ typedef enum { RESA_FP32 = 0, RESA_BF16 = 1 } resa_dtype;
  * sequence, for every KV head. Sequence b's token t lives in page
  * block_table[b * max_blocks_per_seq + t / 16], slot t % 16.
  *
- *   k_pages, v_pages : [num_pages][num_kv_heads][16][head_dim]   (dtype)
+ *   k_pages          : [num_pages][num_kv_heads][16][head_dim]   (dtype), token-major
+ *   v_pages          : [num_pages][num_kv_heads][head_dim][16]   (dtype), channel-major:
+ *                      V[t][c] of the page is at [..][c][t % 16]
  *   desc             : [num_pages][num_kv_heads][2][head_dim]    (dtype)
  *                      [..][0][c] = min over the block's valid tokens of K[., c],
  *                      [..][1][c] = max (the Quest-style block descriptor of

@@ -54,7 +54,7 @@ def test_n_cap_and_sizes(lib):
     p = R.ResaSelectParams(16, 1, 0.1)
     # M = ceil(500/16) = 32 blocks, n = max(16, ceil(3.2)) = 16
     assert lib.resa_n_cap(ctypes.byref(c), ctypes.byref(p)) == 16
-    assert lib.resa_select_workspace_size(ctypes.byref(c)) == 2 * 2 * 32 * 8
+    assert lib.resa_select_workspace_size(ctypes.byref(c)) >= 2 * 2 * 32 * 8  # scores + control block
     assert lib.resa_decode_workspace_size(ctypes.byref(c), 16) > 0
     assert lib.resa_rectify_workspace_size(ctypes.byref(c), 32) > 0
     assert lib.resa_rectify_workspace_size(ctypes.byref(c), 65) == 0

@@ -49,7 +49,7 @@ def _run_loop_parity(w, steps=None, check_all_desc_every=0):
             pos = oc.seq_lens[b] - 1
             page = int(oc.block_table[b, pos // 16])
             assert torch.equal(r.cache.k_pages[page, :, pos % 16].cpu(), k[b]), (t, b)
-            assert torch.equal(r.cache.v_pages[page, :, pos % 16].cpu(), v[b]), (t, b)
+            assert torch.equal(r.cache.v_pages[page, :, :, pos % 16].cpu(), v[b]), (t, b)
             P.assert_desc_equal(r.cache.desc, oc, [page])
         err, nt = P.check_select_and_decode(oc, P.f64(q), w, r.idx, r.count, out, atol)
         worst, ties = max(worst, err), ties + nt
@@ -68,7 +68,7 @@ def _run_loop_parity(w, steps=None, check_all_desc_every=0):
                     pos = L - w.f + i
                     page = int(oc.block_table[b, pos // 16])
                     assert torch.equal(r.cache.k_pages[page, :, pos % 16].cpu(), rk[b, i])
-                    assert torch.equal(r.cache.v_pages[page, :, pos % 16].cpu(), rv[b, i])
+                    assert torch.equal(r.cache.v_pages[page, :, :, pos % 16].cpu(), rv[b, i])
             P.assert_desc_equal(r.cache.desc, oc)
         if check_all_desc_every and (t + 1) % check_all_desc_every == 0:
             P.assert_desc_equal(r.cache.desc, oc)
