@@ -8,8 +8,8 @@
 // reads the K tile (16 tokens x d, token-major) and the V tile (stored
 // channel-major, d x 16 tokens) of one page, 4 KiB each at d = 128 bf16, and
 // serves all G query heads of the group from them, so each selected byte is
-// fetched once per group. The next block's tiles are loaded while the current
-// one is processed.
+// fetched once per group. Two blocks ahead are in flight while one is
+// processed (three rotating register sets, so no copy ever waits on a load).
 //   q.k: lane = 8 * tp + cg holds tokens tp and tp + 8 and channels
 //   cg*8 + 64*k + [0, 8) of K (every 16-byte load covers whole 128-byte lines);
 //   bf16 pairs go through v_dot2 with fp32 accumulation, then a 3-step DPP sum
@@ -18,7 +18,10 @@
 //   logit exceeds it by more than 2^8 (numerator and denominator share every
 //   rescale, so the result is unchanged); each of the 2G (token, head) pairs of
 //   a token pair is exponentiated by one lane and published through LDS.
-//   p.V: lane owns head_dim/64 channels; its V rows are 16 contiguous tokens.
+//   p.V: lane owns head_dim/64 channels; its V rows are 16 contiguous tokens,
+//   so with bf16 the probabilities are rounded to bf16 and multiplied in token
+//   pairs with v_dot2 (fp32 accumulation; the softmax denominator sums the
+//   same rounded values).
 // The 4 wave states are merged through LDS into one split partial (m, l,
 // acc[d]) in fp32; k_decode_combine then merges a group's splits with
 // log-sum-exp weights (a separate kernel, so the hand-off needs no
@@ -196,10 +199,23 @@ __device__ __forceinline__ void store_out(void* out, size_t i, float x) {
 
 template <int G, int D>
 struct DecSmem {
-  float p[kDecWaves][16][G];      // probabilities of the current block, per wave
+  float p[kDecWaves][16][G];       // fp32 cache: probabilities of the current block
+  uint16_t pb[kDecWaves][G][16];   // bf16 cache: the same, rounded, token pairs adjacent
   float m[kDecWaves][G];
   float l[kDecWaves][G];
   float acc[kDecWaves][G][D];
+};
+
+// The K rows (tokens tp, tp + 8) and V rows of one block for one lane.
+template <typename T, int D>
+struct BlockRegs {
+  KRow<T, D> k0, k1;
+  VRows<T, D / 64> v;
+  __device__ void load(const T* kt, const T* vt, int tp, int cg, int lane) {
+    k0.load(kt + tp * D, cg);
+    k1.load(kt + (tp + 8) * D, cg);
+    v.load(vt, lane);
+  }
 };
 
 // grid: x = split, y = KV head, z = sequence; 256 threads.
@@ -208,30 +224,45 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
   constexpr int CPL = D / 64;                      // V channels per lane
   constexpr int PAIRS = 2 * G;                     // (token, head) pairs per token pair
   constexpr int PPL = PAIRS > 8 ? PAIRS / 8 : 1;   // pairs per lane
+  constexpr bool BF16 = sizeof(T) == 2;
   __shared__ DecSmem<G, D> sm;
   const CacheView& c = a.c;
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tp = lane >> 3, cg = lane & 7;
-  const int n = a.count[b];
-  const int first = s * a.bps;
-  const int nblk = min(a.bps, n - first);
-  if (nblk <= 0) return;
-  const int L = c.seq_lens[b];
   const size_t gi = size_t(b) * c.Hkv + g;
+  const int first = s * a.bps;
 
+  // Block ids and page ids of this wave's blocks (first + wave + 4 i), read
+  // before the count is known: indices are clamped into the idx row, the block
+  // table row and the page pool, so every load is in bounds; blocks past the
+  // count are never used.
+  int my_blk = 0, my_page = 0;
+  if (lane * kDecWaves < a.bps) {
+    const int pos = min(first + wave + kDecWaves * lane, a.n_cap - 1);
+    my_blk = min(max(a.idx[gi * a.n_cap + pos], 0), c.maxb - 1);
+    my_page = min(max(c.bt[size_t(b) * c.maxb + my_blk], 0), c.num_pages - 1);
+  }
+  const int n = a.count[b];
+  const int L = c.seq_lens[b];
   QRow<T, D> qr[G];
 #pragma unroll
   for (int h = 0; h < G; ++h)
     qr[h].load(static_cast<const T*>(a.q) + (size_t(b) * c.Hq + size_t(g) * G + h) * D, cg);
 
-  // this wave's blocks: first + wave + 4 * i
-  const int nw = nblk > wave ? (nblk - wave + kDecWaves - 1) / kDecWaves : 0;
-  int my_blk = 0, my_page = 0;
-  if (lane < nw) {
-    my_blk = a.idx[gi * a.n_cap + first + wave + kDecWaves * lane];
-    my_page = c.bt[size_t(b) * c.maxb + my_blk];
+  const T* kbase = static_cast<const T*>(c.k);
+  const T* vbase = static_cast<const T*>(c.v);
+  auto tile = [&](const T* base, int page) { return base + (size_t(page) * c.Hkv + g) * kBlock * D; };
+  BlockRegs<T, D> A, B, C;
+  {
+    const int p0 = __builtin_amdgcn_readlane(my_page, 0);
+    const int p1 = __builtin_amdgcn_readlane(my_page, 1);
+    A.load(tile(kbase, p0), tile(vbase, p0), tp, cg, lane);
+    B.load(tile(kbase, p1), tile(vbase, p1), tp, cg, lane);
   }
+  const int nblk = min(a.bps, n - first);
+  if (nblk <= 0) return;
+  const int nw = nblk > wave ? (nblk - wave + kDecWaves - 1) / kDecWaves : 0;
 
   float m[G], lpart[PPL], acc[G][CPL];
 #pragma unroll
@@ -243,35 +274,21 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
 #pragma unroll
   for (int u = 0; u < PPL; ++u) lpart[u] = 0.f;
 
-  const T* kbase = static_cast<const T*>(c.k);
-  const T* vbase = static_cast<const T*>(c.v);
-  auto tile = [&](const T* base, int page) { return base + (size_t(page) * c.Hkv + g) * kBlock * D; };
-
-  KRow<T, D> k0, k1, nk0, nk1;
-  VRows<T, CPL> vr, nvr;
-  if (nw > 0) {
-    const int page = __builtin_amdgcn_readlane(my_page, 0);
-    k0.load(tile(kbase, page) + tp * D, cg);
-    k1.load(tile(kbase, page) + (tp + 8) * D, cg);
-    vr.load(tile(vbase, page), lane);
-  }
-  for (int it = 0; it < nw; ++it) {
-    const int blk = __builtin_amdgcn_readlane(my_blk, it);
-    if (it + 1 < nw) {
-      const int np = __builtin_amdgcn_readlane(my_page, it + 1);
-      nk0.load(tile(kbase, np) + tp * D, cg);
-      nk1.load(tile(kbase, np) + (tp + 8) * D, cg);
-      nvr.load(tile(vbase, np), lane);
+  // One block: q.k, online softmax, p.V. `spare` receives block it + 2.
+  auto step = [&](int it, BlockRegs<T, D>& cur, BlockRegs<T, D>& spare) {
+    if (it + 2 < nw) {
+      const int np = __builtin_amdgcn_readlane(my_page, it + 2);
+      spare.load(tile(kbase, np), tile(vbase, np), tp, cg, lane);
     }
+    const int blk = __builtin_amdgcn_readlane(my_blk, it);
     const int valid = min(kBlock, L - blk * kBlock);
     const bool ok0 = tp < valid, ok1 = tp + 8 < valid;
-
     float x0[G], x1[G];
     bool need = false;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      x0[h] = ok0 ? sum8(qr[h].dot(k0)) * a.scale_log2 : -__builtin_inff();
-      x1[h] = ok1 ? sum8(qr[h].dot(k1)) * a.scale_log2 : -__builtin_inff();
+      x0[h] = ok0 ? sum8(qr[h].dot(cur.k0)) * a.scale_log2 : -__builtin_inff();
+      x1[h] = ok1 ? sum8(qr[h].dot(cur.k1)) * a.scale_log2 : -__builtin_inff();
       need |= fmaxf(x0[h], x1[h]) > m[h] + kLazyRescale;
     }
     if (__builtin_amdgcn_ballot_w64(need)) {
@@ -299,41 +316,72 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
       if (pr < PAIRS) {
         const int h = pr % G;
         const bool second = pr >= G;
-        float x = x0[0];
+        float x = x0[0], mh = m[0];
 #pragma unroll
         for (int hh = 0; hh < G; ++hh)
-          if (hh == h) x = second ? x1[hh] : x0[hh];
-        float mh = m[0];
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh)
-          if (hh == h) mh = m[hh];
-        const float p = x == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(x - mh);
-        lpart[u] += p;
-        sm.p[wave][second ? tp + 8 : tp][h] = p;
+          if (hh == h) {
+            x = second ? x1[hh] : x0[hh];
+            mh = m[hh];
+          }
+        const float pf = x == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(x - mh);
+        const int t = second ? tp + 8 : tp;
+        if constexpr (BF16) {
+          const uint16_t pbits = f32_to_bf16(pf);  // the value p.V uses; l sums the same value
+          lpart[u] += bf16_to_f32(pbits);
+          sm.pb[wave][h][t] = pbits;
+        } else {
+          lpart[u] += pf;
+          sm.p[wave][t][h] = pf;
+        }
       }
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
-    if (valid < kBlock) vr.mask_tokens(valid);  // slots past the sequence end may hold anything
+    if (valid < kBlock) cur.v.mask_tokens(valid);  // slots past the sequence end may hold anything
+    if constexpr (BF16) {
+      // p.V as bf16 pair dot products: a V row word holds tokens (2i, 2i + 1)
 #pragma unroll
-    for (int t = 0; t < kBlock; ++t) {
-      float pt[G];
+      for (int h = 0; h < G; ++h) {
+        const uint4* pp = reinterpret_cast<const uint4*>(&sm.pb[wave][h][0]);
+        const uint4 p03 = pp[0], p47 = pp[1];
+        const uint32_t pw[8] = {p03.x, p03.y, p03.z, p03.w, p47.x, p47.y, p47.z, p47.w};
 #pragma unroll
-      for (int h = 0; h < G; ++h) pt[h] = sm.p[wave][t][h];
+        for (int cc = 0; cc < CPL; ++cc) {
+          const uint32_t vw[8] = {cur.v.u[cc][0].x, cur.v.u[cc][0].y, cur.v.u[cc][0].z, cur.v.u[cc][0].w,
+                                  cur.v.u[cc][1].x, cur.v.u[cc][1].y, cur.v.u[cc][1].z, cur.v.u[cc][1].w};
+          float sacc = acc[h][cc];
 #pragma unroll
-      for (int cc = 0; cc < CPL; ++cc) {
-        const float vv = vr.get(cc, t);
+          for (int i = 0; i < 8; ++i)
+            sacc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[i]),
+                                                   __builtin_bit_cast(bf16x2_t, vw[i]), sacc, false);
+          acc[h][cc] = sacc;
+        }
+      }
+    } else {
 #pragma unroll
-        for (int h = 0; h < G; ++h) acc[h][cc] = fmaf(pt[h], vv, acc[h][cc]);
+      for (int t = 0; t < kBlock; ++t) {
+        float pt[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) pt[h] = sm.p[wave][t][h];
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc) {
+          const float vv = cur.v.get(cc, t);
+#pragma unroll
+          for (int h = 0; h < G; ++h) acc[h][cc] = fmaf(pt[h], vv, acc[h][cc]);
+        }
       }
     }
     __builtin_amdgcn_wave_barrier();
-    if (it + 1 < nw) {
-      k0 = nk0;
-      k1 = nk1;
-      vr = nvr;
-    }
+  };
+
+  // three rotating buffers: block it in one, it + 1 in the next, it + 2 loading
+  for (int it = 0; it < nw; it += 3) {
+    step(it, A, C);
+    if (it + 1 >= nw) break;
+    step(it + 1, B, A);
+    if (it + 2 >= nw) break;
+    step(it + 2, C, B);
   }
 
   // wave state -> LDS

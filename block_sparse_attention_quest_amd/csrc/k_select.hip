@@ -17,12 +17,12 @@
 // k_topn, grid (KV head, sequence), 1024 threads: n = min(M, max(n_min,
 // ceil(M r))) in IEEE double; the min(n_local, n) newest blocks are always
 // taken; the other places go to the highest scores, ties to the lower index.
-// The candidates' order-preserving 64-bit keys stay in registers. The
-// threshold is found exactly by radix selection with 8-bit digits starting
-// below the common prefix of the candidates' key range (per-wave LDS
-// histograms keep atomic contention inside a wave) until the candidates that
-// share the threshold's prefix number at most 64; one wave then ranks those
-// exactly (key descending, index ascending). Chosen blocks are marked in an LDS
+// The candidates' order-preserving 64-bit keys stay in registers (each thread
+// issues exactly as many score loads as the longest sequence needs). The
+// threshold is found exactly by radix selection with 12-bit digits starting
+// below the common prefix of the candidates' key range (usually one pass)
+// until the candidates that share the threshold's prefix number at most 64;
+// one wave then ranks those exactly (key descending, index ascending). Chosen blocks are marked in an LDS
 // bitmap and compacted in index order, so the output is sorted ascending.
 //
 // The two kernels hand over through the workspace at the kernel boundary: a
@@ -152,9 +152,11 @@ __device__ __forceinline__ uint64_t order_key(double s) {
   return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
 
+constexpr int kTopnBits = 12;
+constexpr int kTopnBins = 1 << kTopnBits;  // 4 bins per thread
+
 struct TopnSmem {
-  int hist[kTopnWaves][256];
-  int tot[256];
+  int hist[kTopnBins];
   uint32_t sel[kBitmapWords];
   uint32_t tie[kBitmapWords];
   uint64_t red_max[kTopnWaves], red_min[kTopnWaves];
@@ -188,7 +190,9 @@ __device__ __forceinline__ int wg_exclusive_scan(int v, int* tmp, int& total) {
   return before + x - v;
 }
 
-// grid: x = KV head, y = sequence; 1024 threads.
+// grid: x = KV head, y = sequence; 1024 threads. EMAX >= ceil(M / 1024) keys
+// per thread, so every thread issues exactly EMAX score loads.
+template <int EMAX>
 __global__ __launch_bounds__(kTopnThreads) void k_topn(const double* __restrict__ scores,
                                                        const int32_t* __restrict__ seq_lens, int maxb,
                                                        int Hkv, resa_select_params p, int32_t* __restrict__ idx,
@@ -203,34 +207,23 @@ __global__ __launch_bounds__(kTopnThreads) void k_topn(const double* __restrict_
   const int keep = min(p.n_local, n);
   const int quota = n - keep;
   const int Mo = M - keep;  // candidates: blocks 0 .. Mo-1
-  const int E = (M + kTopnThreads - 1) / kTopnThreads;
   const size_t gi = size_t(b) * Hkv + g;
   const double* row = scores + gi * maxb;
 
-  // keys of the candidates, block j = e * 1024 + tid. Every load is issued
-  // unconditionally (out-of-range ones re-read block 0, always in the
-  // workspace) so that all of them are in flight at once.
-  uint64_t key[kTopnMaxPerThread];
-  uint64_t kmax = 0, kmin = ~0ull;
-  double sc[kTopnMaxPerThread];
+  // keys of the candidates, block j = e * 1024 + tid (loads issued together;
+  // out-of-range slots re-read block 0 and are ignored)
+  uint64_t key[EMAX];
+  {
+    double sc[EMAX];
 #pragma unroll
-  for (int e = 0; e < kTopnMaxPerThread; ++e) {
-    const int j = e * kTopnThreads + tid;
-    sc[e] = row[(e < E && j < Mo) ? j : 0];
-  }
-#pragma unroll
-  for (int e = 0; e < kTopnMaxPerThread; ++e) {
-    const int j = e * kTopnThreads + tid;
-    key[e] = (e < E && j < Mo) ? order_key(sc[e]) : 0;
-  }
-#pragma unroll
-  for (int e = 0; e < kTopnMaxPerThread; ++e) {
-    const int j = e * kTopnThreads + tid;
-    if (e < E && j < Mo) {
-      kmax = key[e] > kmax ? key[e] : kmax;
-      kmin = key[e] < kmin ? key[e] : kmin;
+    for (int e = 0; e < EMAX; ++e) {
+      const int j = e * kTopnThreads + tid;
+      sc[e] = row[j < Mo ? j : 0];
     }
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) key[e] = order_key(sc[e]);
   }
+  for (int i = tid; i < kTopnBins; i += kTopnThreads) sm.hist[i] = 0;
   for (int i = tid; i < kBitmapWords; i += kTopnThreads) {
     sm.sel[i] = 0;
     sm.tie[i] = 0;
@@ -242,6 +235,14 @@ __global__ __launch_bounds__(kTopnThreads) void k_topn(const double* __restrict_
   uint64_t prefix = 0, mask = 0;
   int k = quota;
   if (quota > 0) {
+    uint64_t kmax = 0, kmin = ~0ull;
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) {
+      if (e * kTopnThreads + tid < Mo) {
+        kmax = key[e] > kmax ? key[e] : kmax;
+        kmin = key[e] < kmin ? key[e] : kmin;
+      }
+    }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
       const uint64_t x = __shfl_xor(kmax, o, 64), y = __shfl_xor(kmin, o, 64);
@@ -263,48 +264,40 @@ __global__ __launch_bounds__(kTopnThreads) void k_topn(const double* __restrict_
     prefix = kmax & mask;
     int gsize = Mo;  // every candidate lies in [kmin, kmax], so shares the prefix
     int bits_left = 64 - plen;
+    bool first = true;
     while (gsize > kRankGroup && gsize != k && bits_left > 0) {
-      const int nb = bits_left < 8 ? bits_left : 8;
+      const int nb = bits_left < kTopnBits ? bits_left : kTopnBits;
       const int shift = bits_left - nb;
       const int nbins = 1 << nb;
-      for (int i = tid; i < kTopnWaves * 256; i += kTopnThreads) (&sm.hist[0][0])[i] = 0;
-      __syncthreads();
+      if (!first) {
+        for (int i = tid; i < kTopnBins; i += kTopnThreads) sm.hist[i] = 0;
+        __syncthreads();
+      }
+      first = false;
 #pragma unroll
-      for (int e = 0; e < kTopnMaxPerThread; ++e) {
-        const int j = e * kTopnThreads + tid;
-        if (e < E && j < Mo && (key[e] & mask) == prefix)
-          atomicAdd(&sm.hist[wave][int(key[e] >> shift) & (nbins - 1)], 1);
+      for (int e = 0; e < EMAX; ++e) {
+        if (e * kTopnThreads + tid < Mo && (key[e] & mask) == prefix)
+          atomicAdd(&sm.hist[int(key[e] >> shift) & (nbins - 1)], 1);
       }
       __syncthreads();
-      if (tid < 256) {
-        int t = 0;
+      // thread t owns the 4 digits nbins-1-4t .. nbins-4-4t (from the top)
+      int h[4], mine = 0;
 #pragma unroll
-        for (int w = 0; w < kTopnWaves; ++w) t += sm.hist[w][tid];
-        sm.tot[tid] = t;
+      for (int u = 0; u < 4; ++u) {
+        const int d = nbins - 1 - (4 * tid + u);
+        h[u] = d >= 0 ? sm.hist[d] : 0;
+        mine += h[u];
       }
-      __syncthreads();
-      if (tid < 64) {
-        // lane owns digits 4 lane .. 4 lane + 3; elements with larger digits
-        // come from a suffix sum over the lanes above
-        const int d0 = 4 * tid;
-        const int h[4] = {sm.tot[d0], sm.tot[d0 + 1], sm.tot[d0 + 2], sm.tot[d0 + 3]};
-        const int mine = h[0] + h[1] + h[2] + h[3];
-        int suf = mine;
+      int total;
+      int above = wg_exclusive_scan(mine, sm.scan, total);
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const int y = __shfl_down(suf, o, 64);
-          if (tid + o < 64) suf += y;
+      for (int u = 0; u < 4; ++u) {
+        if (above < k && above + h[u] >= k) {
+          sm.digit = nbins - 1 - (4 * tid + u);
+          sm.k_rem = k - above;
+          sm.gsize = h[u];
         }
-        int above = suf - mine;
-#pragma unroll
-        for (int u = 3; u >= 0; --u) {
-          if (above < k && above + h[u] >= k) {
-            sm.digit = d0 + u;
-            sm.k_rem = k - above;
-            sm.gsize = h[u];
-          }
-          above += h[u];
-        }
+        above += h[u];
       }
       __syncthreads();
       prefix |= uint64_t(sm.digit) << shift;
@@ -318,9 +311,9 @@ __global__ __launch_bounds__(kTopnThreads) void k_topn(const double* __restrict_
       if (tid == 0) sm.gcount = 0;
       __syncthreads();
 #pragma unroll
-      for (int e = 0; e < kTopnMaxPerThread; ++e) {
+      for (int e = 0; e < EMAX; ++e) {
         const int j = e * kTopnThreads + tid;
-        if (e < E && j < Mo && (key[e] & mask) == prefix) {
+        if (j < Mo && (key[e] & mask) == prefix) {
           const int s = atomicAdd(&sm.gcount, 1);
           sm.gk[s] = key[e];
           sm.gj[s] = j;
@@ -345,9 +338,9 @@ __global__ __launch_bounds__(kTopnThreads) void k_topn(const double* __restrict_
   __syncthreads();
   // mark the chosen blocks
 #pragma unroll
-  for (int e = 0; e < kTopnMaxPerThread; ++e) {
+  for (int e = 0; e < EMAX; ++e) {
     const int j = e * kTopnThreads + tid;
-    if (e >= E || j >= M) continue;
+    if (j >= M) continue;
     bool s = false, t = false;
     if (j >= Mo) {
       s = true;
@@ -387,6 +380,25 @@ __global__ __launch_bounds__(kTopnThreads) void k_topn(const double* __restrict_
   }
 }
 
+hipError_t launch_topn(const CacheView& c, const resa_select_params& p, int32_t* idx, int32_t* count,
+                       int n_cap, const double* scores, hipStream_t s) {
+  const int mmax = (c.max_seq_len + kBlock - 1) / kBlock;
+  const int e = (mmax + kTopnThreads - 1) / kTopnThreads;
+  dim3 grid(c.Hkv, c.B);
+#define RESA_TOPN(E) hipLaunchKernelGGL(k_topn<E>, grid, dim3(kTopnThreads), 0, s, scores, c.seq_lens, c.maxb, \
+                                        c.Hkv, p, idx, count, n_cap)
+  if (e <= 2) RESA_TOPN(2);
+  else if (e <= 4) RESA_TOPN(4);
+  else if (e <= 8) RESA_TOPN(8);
+  else if (e <= 12) RESA_TOPN(12);
+  else if (e <= 16) RESA_TOPN(16);
+  else if (e <= 20) RESA_TOPN(20);
+  else if (e <= 24) RESA_TOPN(24);
+  else RESA_TOPN(32);
+#undef RESA_TOPN
+  return hipGetLastError();
+}
+
 template <typename T, int D>
 hipError_t launch_select_t(const CacheView& c, const void* q, const resa_select_params& p, int32_t* idx,
                            int32_t* count, int n_cap, double* scores, hipStream_t s) {
@@ -394,10 +406,7 @@ hipError_t launch_select_t(const CacheView& c, const void* q, const resa_select_
   hipLaunchKernelGGL((k_score<T, D>), g1, dim3(kScoreThreads), 0, s, c, q, scores);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 g2(c.Hkv, c.B);
-  hipLaunchKernelGGL(k_topn, g2, dim3(kTopnThreads), 0, s, scores, c.seq_lens, c.maxb, c.Hkv, p, idx, count,
-                     n_cap);
-  return hipGetLastError();
+  return launch_topn(c, p, idx, count, n_cap, scores, s);
 }
 
 }  // namespace
