@@ -19,6 +19,8 @@
 // kernel merges the chunks with log-sum-exp weights.
 //
 // fp32 path (k_rect_valu): one wave per (sequence, row, head), plain VALU.
+#include <type_traits>
+
 #include "resa_internal.h"
 
 namespace resa {
@@ -33,21 +35,71 @@ struct RectArgs {
   float* part_acc;  // [B][Hkv][splits][rows_pad][D]
 };
 
-template <int D>
-struct RectSmem {
-  static constexpr int KS = D + 8;               // K row stride (elements)
-  static constexpr int VS = kRectTileKeys + 8;   // V^T row stride (elements)
-  uint16_t k[kRectTileKeys * KS];
-  uint16_t vt[D * VS];
-};
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(1))) const void* global_ptr_t;
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// grid: x = key chunk, y = KV head, z = sequence; 256 threads.
-template <int D, int TPW>
-__global__ __launch_bounds__(256) void k_rect_mfma(RectArgs a) {
+// A 16-byte zero piece: the source of every tile piece that lies past the end of
+// the keys, so that such LDS slots hold zeros rather than whatever the cache
+// slot holds.
+__device__ uint4 kZeroPiece[1];
+
+// Wait until at most N vector-memory instructions of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt(((N >> 4) & 3) << 14 | (0xF << 8) | (7 << 4) | (N & 15));
+}
+
+constexpr int kMaxChunkPages = 1024;  // keys per split <= 16384
+
+// Tile stages live in separate LDS arrays, one per stage, and the tile loop is
+// unrolled by the stage count, so every access names one array at compile time.
+// The compiler can then tell that reading one stage does not depend on the
+// direct-to-LDS loads still in flight into the others.
+//   K stage: [32 keys][D/8 pieces of 8 channels]; piece c of key r sits at
+//            position c ^ (r % (D/8)) of its row (XOR swizzle: the 32 rows read
+//            at one column by an MFMA operand load hit distinct banks).
+//   V stage: [4 groups of 8 keys][D channels] pieces; piece (q, ch) holds channel
+//            ch of keys 8q .. 8q + 7 (V page tiles are channel-major in HBM).
+#define RESA_STAGE_DECL(i) __shared__ uint4 sk##i[PIECES], sv##i[PIECES]
+template <int S>
+__device__ __forceinline__ uint4* pick(uint4* a0, uint4* a1, uint4* a2, uint4* a3, uint4* a4, uint4* a5,
+                                       uint4* a6, uint4* a7) {
+  if constexpr (S == 0) return a0;
+  else if constexpr (S == 1) return a1;
+  else if constexpr (S == 2) return a2;
+  else if constexpr (S == 3) return a3;
+  else if constexpr (S == 4) return a4;
+  else if constexpr (S == 5) return a5;
+  else if constexpr (S == 6) return a6;
+  else return a7;
+}
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// grid: x = key chunk, y = KV head, z = sequence; NWV waves. Wave w owns query
+// rows 32w .. 32w + 31 (a wave past G * f rows only loads). NS tile stages.
+template <int D, int NWV, int NS>
+__global__ __launch_bounds__(64 * NWV, 2) void k_rect_mfma(RectArgs a) {
+  constexpr int NT = 64 * NWV;
   constexpr int KSTEPS = D / 16;   // 16-deep k-steps of the score product
   constexpr int DT = D / 32;       // 32-wide output column tiles
-  constexpr int EPT = D / 8;       // elements per thread of a tile row load
-  __shared__ RectSmem<D> sm;
+  constexpr int CPR = D / 8;       // pieces per K row
+  constexpr int PIECES = kRectTileKeys * D / 8;  // per tile, K and V each
+  constexpr int INSTR = 2 * PIECES / 64;         // wave-wide loads per tile
+  constexpr int LPT = INSTR / NWV;               // loads per thread per tile
+  static_assert(INSTR % NWV == 0, "tile loads must split evenly over the waves");
+  static_assert(NS >= 2 && NS <= 8, "2 .. 8 stages");
+  constexpr float kLazy = 8.0f;    // log2 units
+  RESA_STAGE_DECL(0); RESA_STAGE_DECL(1); RESA_STAGE_DECL(2); RESA_STAGE_DECL(3);
+  RESA_STAGE_DECL(4); RESA_STAGE_DECL(5); RESA_STAGE_DECL(6); RESA_STAGE_DECL(7);
+  __shared__ int pages[kMaxChunkPages];
   const CacheView& c = a.c;
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -55,177 +107,207 @@ __global__ __launch_bounds__(256) void k_rect_mfma(RectArgs a) {
   const int key_lo = s * a.chunk;
   if (key_lo >= L) return;
   const int key_hi = min(L, key_lo + a.chunk);
+  const int ntiles = (key_hi - key_lo + kRectTileKeys - 1) / kRectTileKeys;
   const int G = c.G;
   const int col = lane & 31, half = lane >> 5;
+  const bool has_rows = wave * 32 < a.rows;  // wave-uniform
+  const int first_masked = L - a.f;          // keys from here on are seen by some rows only
 
-  // query rows of this lane (one per owned row tile), as MFMA B operands
-  bf16x8_t qreg[TPW][KSTEPS];
-  int limit[TPW];  // last key position the row may see (-1: padding row)
-#pragma unroll
-  for (int u = 0; u < TPW; ++u) {
-    const int r = (wave + 4 * u) * 32 + col;
+  // page ids of the chunk
+  const int page0 = key_lo >> 4;
+  const int npages = (key_hi - 1) / kBlock - page0 + 1;
+  for (int i = tid; i < npages; i += NT) pages[i] = c.bt[size_t(b) * c.maxb + page0 + i];
+
+  // this lane's query row as MFMA B operands (S^T = K Q^T)
+  bf16x8_t qreg[KSTEPS];
+  int limit;  // last key position the row may see (-1: padding row)
+  {
+    const int r = wave * 32 + col;
     const bool live = r < a.rows;
     const int i = r / G, h = r % G;
-    limit[u] = live ? L - a.f + i : -1;
+    limit = live ? L - a.f + i : -1;
     const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
-                           ((size_t(b) * a.f + i) * c.Hq + size_t(g) * G + h) * D;
+                           ((size_t(b) * a.f + (live ? i : 0)) * c.Hq + size_t(g) * G + (live ? h : 0)) * D;
+    // a padding row reads row 0: all of its keys are masked and it writes nothing
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      uint4 w = make_uint4(0, 0, 0, 0);
-      if (live) w = *reinterpret_cast<const uint4*>(qrow + ks * 16 + 8 * half);
-      qreg[u][ks] = __builtin_bit_cast(bf16x8_t, w);
-    }
+    for (int ks = 0; ks < KSTEPS; ++ks)
+      qreg[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qrow + ks * 16 + 8 * half));
   }
-
-  f32x16_t o[TPW][DT];
-  float m[TPW], lsum[TPW];
-#pragma unroll
-  for (int u = 0; u < TPW; ++u) {
-    m[u] = -__builtin_inff();
-    lsum[u] = 0.f;
-#pragma unroll
-    for (int t = 0; t < DT; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[u][t][r] = 0.f;
-  }
+  wait_vmcnt<0>();  // query rows and page ids are in before any tile load is issued
+  __syncthreads();  // page ids visible
 
   const uint16_t* kb = static_cast<const uint16_t*>(c.k);
   const uint16_t* vb = static_cast<const uint16_t*>(c.v);
-  // K: thread -> (key lk, columns lc .. lc + EPT) of the token-major K rows.
-  // V: the page tiles are channel-major (d x 16 tokens); thread -> 16-byte
-  // pieces u = tid + 256 e: page pg of the tile, channel ch, 8 tokens at 8 vh.
-  const int lk = tid / 8;
-  const int lc = (tid % 8) * EPT;
-  uint4 kreg[EPT / 8], vreg[EPT / 8];
-  // Keys past the chunk end are read from the chunk's first key (always valid)
-  // and zeroed, so uninitialised slots never reach the products.
-  auto load_tile = [&](int base) {
-    {
-      const int key = base + lk;
-      const bool ok = key < key_hi;
-      const int kk = ok ? key : key_lo;
-      const int page = c.bt[size_t(b) * c.maxb + (kk >> 4)];
-      const size_t off = ((size_t(page) * c.Hkv + g) * kBlock + (kk & 15)) * D + lc;
-      const uint32_t keep = ok ? 0xffffffffu : 0u;
+  // Issue the LPT direct-to-LDS loads of tile ti into the given stage arrays.
+  auto issue_tile = [&](int ti, uint4* kst, uint4* vst) {
+    const int base = key_lo + ti * kRectTileKeys;
 #pragma unroll
-      for (int e = 0; e < EPT / 8; ++e) {
-        const uint4 kv = *reinterpret_cast<const uint4*>(kb + off + 8 * e);
-        kreg[e] = make_uint4(kv.x & keep, kv.y & keep, kv.z & keep, kv.w & keep);
+    for (int li = 0; li < LPT; ++li) {
+      const int ins = li * NWV + wave;  // wave-uniform
+      const void* src;
+      uint4* dst;
+      if (ins < INSTR / 2) {  // K pieces
+        const int pidx = ins * 64 + lane;
+        const int key = pidx / CPR, cpos = pidx % CPR;
+        const int cl = cpos ^ (key % CPR);
+        const int kg = base + key;
+        src = kg < key_hi ? static_cast<const void*>(
+                                kb + ((size_t(pages[(kg >> 4) - page0]) * c.Hkv + g) * kBlock + (kg & 15)) * D + cl * 8)
+                          : static_cast<const void*>(kZeroPiece);
+        dst = kst + ins * 64;
+      } else {  // V pieces
+        const int pidx = (ins - INSTR / 2) * 64 + lane;
+        const int q = pidx / D, ch = pidx % D;
+        const int t0 = base + 8 * q;
+        src = t0 < key_hi ? static_cast<const void*>(
+                                vb + ((size_t(pages[(t0 >> 4) - page0]) * c.Hkv + g) * D + ch) * kBlock + (t0 & 15))
+                          : static_cast<const void*>(kZeroPiece);
+        dst = vst + (ins - INSTR / 2) * 64;
       }
-    }
-#pragma unroll
-    for (int e = 0; e < EPT / 8; ++e) {
-      const int u = tid + 256 * e;
-      const int pg = u / (2 * D), ch = (u % (2 * D)) / 2, vh = u % 2;
-      const int t0 = base + pg * 16 + vh * 8;  // key of the first of the 8 tokens
-      const int kk = t0 < key_hi ? t0 : key_lo;
-      const int page = c.bt[size_t(b) * c.maxb + (kk >> 4)];
-      const size_t off = ((size_t(page) * c.Hkv + g) * D + ch) * kBlock + (t0 < key_hi ? vh * 8 : 0);
-      uint4 vv = *reinterpret_cast<const uint4*>(vb + off);
-      const int nvalid = key_hi - t0;  // tokens of the 8 that exist
-      if (nvalid < 8) {
-        const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
-        uint32_t o[4];
-#pragma unroll
-        for (int x = 0; x < 4; ++x)
-          o[x] = w[x] & ((2 * x < nvalid ? 0x0000ffffu : 0u) | (2 * x + 1 < nvalid ? 0xffff0000u : 0u));
-        vv = make_uint4(o[0], o[1], o[2], o[3]);
-      }
-      vreg[e] = vv;
+      __builtin_amdgcn_global_load_lds((global_ptr_t)src, (lds_ptr_t)dst, 16, 0, 0);
     }
   };
 
-  load_tile(key_lo);
-  for (int base = key_lo; base < key_hi; base += kRectTileKeys) {
-    __syncthreads();  // previous tile fully consumed
+  f32x16_t o[DT];
 #pragma unroll
-    for (int e = 0; e < EPT / 8; ++e) {
-      *reinterpret_cast<uint4*>(&sm.k[lk * RectSmem<D>::KS + lc + 8 * e]) = kreg[e];
-      const int u = tid + 256 * e;
-      const int pg = u / (2 * D), ch = (u % (2 * D)) / 2, vh = u % 2;
-      *reinterpret_cast<uint4*>(&sm.vt[ch * RectSmem<D>::VS + pg * 16 + vh * 8]) = vreg[e];
-    }
-    __syncthreads();
-    if (base + kRectTileKeys < key_hi) load_tile(base + kRectTileKeys);
+  for (int t = 0; t < DT; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
+  float m = -__builtin_inff(), lsum = 0.f;
 
+  auto compute = [&](int ti, const uint4* kst, const uint4* vst) {
+    const int base = key_lo + ti * kRectTileKeys;
+    f32x16_t sacc;
 #pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-      if ((wave + 4 * u) * 32 >= a.rows) continue;  // wave-uniform
-      f32x16_t sacc;
+    for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+    bf16x8_t ak[KSTEPS];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+    for (int ks = 0; ks < KSTEPS; ++ks)
+      ak[ks] = __builtin_bit_cast(bf16x8_t, kst[col * CPR + ((2 * ks + half) ^ (col % CPR))]);
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        const bf16x8_t ak =
-            *reinterpret_cast<const bf16x8_t*>(&sm.k[col * RectSmem<D>::KS + ks * 16 + 8 * half]);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[u][ks], sacc, 0, 0, 0);
-      }
-      // lane holds keys 8*(r/4) + 4*half + r%4 of query row `col`
-      float x[16];
-      float tmax = -__builtin_inff();
+    for (int ks = 0; ks < KSTEPS; ++ks)
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[ks], qreg[ks], sacc, 0, 0, 0);
+    // lane holds keys base + 8 (r/4) + 4 half + r%4 of query row `col`
+    float x[16];
+    if (base + kRectTileKeys > first_masked || base + kRectTileKeys > key_hi) {  // wave-uniform
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = base + 8 * (r / 4) + 4 * half + (r % 4);
-        x[r] = (key < key_hi && key <= limit[u]) ? sacc[r] * a.scale_log2 : -__builtin_inff();
-        tmax = fmaxf(tmax, x[r]);
+        x[r] = (key < key_hi && key <= limit) ? sacc[r] * a.scale_log2 : -__builtin_inff();
       }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float mnew = fmaxf(m[u], tmax);
-      const float alpha = mnew == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f(m[u] - mnew);
-      float p[16];
-      float psum = 0.f;
+    } else {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        p[r] = x[r] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(x[r] - mnew);
-        psum += p[r];
+      for (int r = 0; r < 16; ++r) x[r] = limit >= 0 ? sacc[r] * a.scale_log2 : -__builtin_inff();
+    }
+    float tmax = x[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, x[r]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    // the running max moves only when a logit exceeds it by more than 2^8;
+    // numerator and denominator share every rescale
+    if (__builtin_amdgcn_ballot_w64(tmax > m + kLazy)) {
+      const float mnew = fmaxf(m, tmax);
+      const float alpha = m == -__builtin_inff() ? (mnew == -__builtin_inff() ? 1.f : 0.f)
+                                                 : __builtin_amdgcn_exp2f(m - mnew);
+      lsum *= alpha;
+#pragma unroll
+      for (int t = 0; t < DT; ++t) o[t] *= alpha;
+      m = mnew;
+    }
+    float p[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      p[r] = x[r] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(x[r] - m);
+      lsum += p[r];
+    }
+    bf16x8_t pb[2];
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      uint32_t w[4];
+#pragma unroll
+      for (int x2 = 0; x2 < 4; ++x2) {
+        const f32x2_t pr = {p[8 * k2 + 2 * x2], p[8 * k2 + 2 * x2 + 1]};
+        w[x2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2_t));
       }
-      lsum[u] = lsum[u] * alpha + psum;
-      m[u] = mnew;
-      bf16x8_t pb[2];
+      pb[k2] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+    }
+#pragma unroll
+    for (int t = 0; t < DT; ++t) {
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
-        uint32_t w[4];
-#pragma unroll
-        for (int x2 = 0; x2 < 4; ++x2)
-          w[x2] = uint32_t(f32_to_bf16(p[8 * k2 + 2 * x2])) | (uint32_t(f32_to_bf16(p[8 * k2 + 2 * x2 + 1])) << 16);
-        pb[k2] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
-      }
-#pragma unroll
-      for (int t = 0; t < DT; ++t) {
-        o[u][t] *= alpha;
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          const uint16_t* vrow = &sm.vt[(t * 32 + col) * RectSmem<D>::VS + k2 * 16 + 4 * half];
-          const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
-          const bf16x8_t av = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
-          o[u][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[k2], o[u][t], 0, 0, 0);
-        }
+        // keys 16 k2 + 4 half + [0, 4) from group 2 k2, + 8 from group 2 k2 + 1
+        const uint2 lo = reinterpret_cast<const uint2*>(&vst[(2 * k2) * D + t * 32 + col])[half];
+        const uint2 hi = reinterpret_cast<const uint2*>(&vst[(2 * k2 + 1) * D + t * 32 + col])[half];
+        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[k2], o[t], 0, 0, 0);
       }
     }
+  };
+
+  // Pipeline: NS - 1 tiles are in flight. At step t the wave waits for its own
+  // loads of tile t, a barrier makes everyone's visible, tile t + NS - 1 is
+  // requested into the stage tile t - 1 used (every wave finished computing it
+  // before this barrier), and tile t is computed.
+  static_for<0, NS - 1>([&](auto S) {
+    if (S.value < ntiles)
+      issue_tile(S.value, pick<S.value>(sk0, sk1, sk2, sk3, sk4, sk5, sk6, sk7),
+                 pick<S.value>(sv0, sv1, sv2, sv3, sv4, sv5, sv6, sv7));
+  });
+  for (int t0 = 0; t0 < ntiles; t0 += NS) {
+    static_for<0, NS>([&](auto S) {
+      const int t = t0 + S.value;
+      if (t >= ntiles) return;
+      constexpr int SN = (S.value + NS - 1) % NS;  // stage of tile t + NS - 1
+      uint4* kcur = pick<S.value>(sk0, sk1, sk2, sk3, sk4, sk5, sk6, sk7);
+      uint4* vcur = pick<S.value>(sv0, sv1, sv2, sv3, sv4, sv5, sv6, sv7);
+      const int ahead = min(NS - 2, ntiles - 1 - t);  // tiles after t already requested
+      if (ahead >= NS - 2) wait_vmcnt<(NS - 2) * LPT>();
+      else if (ahead <= 0) wait_vmcnt<0>();
+      else if (ahead == 1) wait_vmcnt<LPT>();
+      else if (ahead == 2) wait_vmcnt<2 * LPT>();
+      else if (ahead == 3) wait_vmcnt<3 * LPT>();
+      else if (ahead == 4) wait_vmcnt<4 * LPT>();
+      else wait_vmcnt<0>();
+      // Every wave has its own loads of tile t complete; the bare barrier (no
+      // fence) then makes the whole tile visible without draining the loads of
+      // later tiles that are still in flight. The memory clobber keeps the
+      // compiler from moving LDS accesses across it.
+      asm volatile("s_barrier" ::: "memory");
+      if (t == ntiles - 1 && (key_hi & 7) != 0) {
+        // the last V group holds keys past the end: zero them
+        const int q = ((key_hi - key_lo) - t * kRectTileKeys) / 8;
+        const int from = key_hi & 7;
+        for (int ch = tid; ch < D; ch += NT) {
+          uint16_t* e = reinterpret_cast<uint16_t*>(&vcur[q * D + ch]);
+          for (int x2 = from; x2 < 8; ++x2) e[x2] = 0;
+        }
+        __syncthreads();
+      }
+      if (t + NS - 1 < ntiles)
+        issue_tile(t + NS - 1, pick<SN>(sk0, sk1, sk2, sk3, sk4, sk5, sk6, sk7),
+                   pick<SN>(sv0, sv1, sv2, sv3, sv4, sv5, sv6, sv7));
+      if (has_rows) compute(t, kcur, vcur);
+    });
   }
 
-  // write partials: lane holds O^T[dcol][row col] for dcol = 32t + 8(r/4) + 4 half + r%4
-#pragma unroll
-  for (int u = 0; u < TPW; ++u) {
-    const int rt = wave + 4 * u;
-    if (rt * 32 >= a.rows) continue;
-    const int r = rt * 32 + col;
-    const float ltot = lsum[u] + __shfl_xor(lsum[u], 32, 64);
-    const size_t slot = ((size_t(b) * c.Hkv + g) * a.splits + s) * a.rows_pad + r;
-    if (half == 0) {
-      a.part_ml[slot * 2 + 0] = m[u];
-      a.part_ml[slot * 2 + 1] = ltot;
-    }
-    float* dst = a.part_acc + slot * D;
-#pragma unroll
-    for (int t = 0; t < DT; ++t)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        *reinterpret_cast<float4*>(dst + t * 32 + 8 * q4 + 4 * half) =
-            make_float4(o[u][t][4 * q4 + 0], o[u][t][4 * q4 + 1], o[u][t][4 * q4 + 2], o[u][t][4 * q4 + 3]);
+  // partials: lane holds O^T[dcol][row col] for dcol = 32t + 8(r/4) + 4 half + r%4
+  if (!has_rows) return;
+  const int r = wave * 32 + col;
+  const float ltot = lsum + __shfl_xor(lsum, 32, 64);
+  const size_t slot = ((size_t(b) * c.Hkv + g) * a.splits + s) * a.rows_pad + r;
+  if (half == 0) {
+    a.part_ml[slot * 2 + 0] = m;
+    a.part_ml[slot * 2 + 1] = ltot;
   }
+  float* dst = a.part_acc + slot * D;
+#pragma unroll
+  for (int t = 0; t < DT; ++t)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4)
+      *reinterpret_cast<float4*>(dst + t * 32 + 8 * q4 + 4 * half) =
+          make_float4(o[t][4 * q4 + 0], o[t][4 * q4 + 1], o[t][4 * q4 + 2], o[t][4 * q4 + 3]);
 }
+#undef RESA_STAGE_DECL
 
 template <typename T>
 __device__ __forceinline__ void store_out(void* out, size_t i, float x) {
@@ -330,16 +412,18 @@ __global__ __launch_bounds__(64) void k_rect_valu(RectArgs a, void* __restrict__
   for (int e = 0; e < D / 64; ++e) store_out<T>(out, oo + lane + 64 * e, acc[e] / l);
 }
 
+template <int D, int NWV, int NS>
+hipError_t launch_mfma_t(const RectArgs& a, hipStream_t st) {
+  const CacheView& c = a.c;
+  dim3 grid(a.splits, c.Hkv, c.B);
+  hipLaunchKernelGGL((k_rect_mfma<D, NWV, NS>), grid, dim3(64 * NWV), 0, st, a);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_mfma(const RectArgs& a, void* out, hipStream_t st) {
   const CacheView& c = a.c;
-  dim3 grid(a.splits, c.Hkv, c.B);
-  const int tiles = a.rows_pad / 32;
-  if (tiles <= 4)
-    hipLaunchKernelGGL((k_rect_mfma<D, 1>), grid, dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL((k_rect_mfma<D, 2>), grid, dim3(256), 0, st, a);
-  hipError_t e = hipGetLastError();
+  hipError_t e = a.rows_pad <= 128 ? launch_mfma_t<D, 4, 4>(a, st) : launch_mfma_t<D, 8, 8>(a, st);
   if (e != hipSuccess) return e;
   dim3 g2((a.rows + 3) / 4, c.Hkv, c.B);
   hipLaunchKernelGGL((k_rect_combine<uint16_t, D>), g2, dim3(256), 0, st, a, out);
@@ -357,7 +441,7 @@ RectPlan plan_rectify(const CacheView& c, int f) {
   long chunk = (keys + 1535) / 1536;
   chunk = (chunk + 255) / 256 * 256;
   if (chunk < 256) chunk = 256;
-  if (chunk > 16384) chunk = 16384;
+  if (chunk > 16384) chunk = 16384;  // = kMaxChunkPages pages
   p.chunk = int(chunk);
   p.splits = (c.max_seq_len + p.chunk - 1) / p.chunk;
   return p;
