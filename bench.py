@@ -28,7 +28,7 @@ if ROOT not in sys.path:
 METRIC = "GBSA decode steps/s + achieved HBM GB/s at 128K ctx (32q/8kv, d=128)"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
-BREAKDOWN_STEPS = 32
+MEASURE_STEPS = 64
 
 
 def _workloads():
@@ -67,6 +67,24 @@ def rectify_work(w, L_list, f):
     kv = sum(Hkv * L * 2 * d * e for L in L_list)
     flops = sum(4 * d * Hq * (f * (L - f) + f * (f + 1) // 2) for L in L_list)
     return kv, flops
+
+
+def decode_traffic(w):
+    """HBM bytes per resa_sparse_decode launch from the rocprofv3 FETCH_SIZE /
+    WRITE_SIZE runs recorded under profiles/ (scaled by the copy-kernel
+    calibration recorded with them); None if they were taken on another
+    workload or on a different version of the decode kernels."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic_decode_gqa128k_b4.json")
+    src = os.path.join(ROOT, "block_sparse_attention_quest_amd", "csrc", "k_decode.hip")
+    try:
+        rec = json.load(open(path))
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != digest or rec.get("workload") != w.name:
+        return None
+    return int(rec["bytes_per_launch"])
 
 
 def n_for(M, w):
@@ -151,6 +169,8 @@ def main():
     ap.add_argument("--workload", default="gqa_128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the hot path here is the per-GPU kernel; "
@@ -165,7 +185,7 @@ def main():
     torch.cuda.set_device(0)
     K, Wu = args.steps, args.warmup
     base = _workloads()[args.workload]()
-    w = base.replace(steps=Wu + K + BREAKDOWN_STEPS)
+    w = base.replace(steps=Wu + K + MEASURE_STEPS)
     t_setup = time.perf_counter()
     print(f"[bench] setting up {w.name}: batch {w.batch}, prefill {w.prefill_lens[0]}, steps {w.steps}",
           file=sys.stderr, flush=True)
@@ -178,6 +198,17 @@ def main():
     print(f"[bench] setup {time.perf_counter() - t_setup:.1f}s", file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream()
+    if args.copy_probe_mb > 0:
+        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE counters give
+        # the factor between counted and actual HBM bytes on this device
+        n = args.copy_probe_mb << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+        junk = torch.empty(512 << 20, dtype=torch.uint8, device="cuda").fill_(0)  # evict src from the caches
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst, junk
 
     def step(t, ev=None):
         if ev is not None:
@@ -192,61 +223,58 @@ def main():
         step(t)
     torch.cuda.synchronize()
 
-    # ---- timed region: K whole steps, decode launches bracketed by events ----
-    dec_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    sel_ev = []
+    def step_calls(t, ev=None):
+        """One whole step through the C ABI; with `ev`, events bracket every call."""
+        r.set_step_lens(t + 1)
+        q = r.step_inputs["q"][t]
+        if ev is not None:
+            ev[0].record(stream)
+        R.resa_update_descriptors(r.cache, r.step_inputs["k"][t], r.step_inputs["v"][t], 1)
+        if ev is not None:
+            ev[1].record(stream)
+        R.resa_select_blocks(r.cache, q, r.params, r.idx, r.count, r.n_cap, r.ws)
+        if ev is not None:
+            ev[2].record(stream)
+        R.resa_sparse_decode(r.cache, q, r.idx, r.count, r.n_cap, r.out, r.ws, r.scale)
+        if ev is not None:
+            ev[3].record(stream)
+        if t in rect_in:
+            if ev is not None:
+                ev[4].record(stream)
+            r.rectify(t, *rect_in[t])
+            if ev is not None:
+                ev[5].record(stream)
+
+    # ---- timed region: K whole steps; events only at its two ends ----
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
     for i in range(K):
-        t = Wu + i
-        r.set_step_lens(t + 1)
-        q = r.step_inputs["q"][t]
-        R.resa_update_descriptors(r.cache, r.step_inputs["k"][t], r.step_inputs["v"][t], 1)
-        a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        R.resa_select_blocks(r.cache, q, r.params, r.idx, r.count, r.n_cap, r.ws)
-        b_.record(stream)
-        sel_ev.append((a, b_))
-        dec_ev[i][0].record(stream)
-        R.resa_sparse_decode(r.cache, q, r.idx, r.count, r.n_cap, r.out, r.ws, r.scale)
-        dec_ev[i][1].record(stream)
-        if t in rect_in:
-            r.rectify(t, *rect_in[t])
+        step_calls(Wu + i)
     e1.record(stream)
     torch.cuda.synchronize()
     total_ms = e0.elapsed_time(e1)
     ms_per_step = total_ms / K
-    dec_ms = sum(x.elapsed_time(y) for x, y in dec_ev) / K
-    sel_ms = sum(x.elapsed_time(y) for x, y in sel_ev) / K
 
-    # ---- stage breakdown (after the timed region) ----
-    times = {"append": [], "select": [], "decode": [], "rectify": []}
-    for i in range(BREAKDOWN_STEPS):
+    # ---- per-call durations: MEASURE_STEPS more steps, HIP events around every
+    # call on the launch stream, queued without per-step synchronisation ----
+    evs = []
+    for i in range(MEASURE_STEPS):
         t = Wu + K + i
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-        r.set_step_lens(t + 1)
-        q = r.step_inputs["q"][t]
-        ev[0].record(stream)
-        R.resa_update_descriptors(r.cache, r.step_inputs["k"][t], r.step_inputs["v"][t], 1)
-        ev[1].record(stream)
-        R.resa_select_blocks(r.cache, q, r.params, r.idx, r.count, r.n_cap, r.ws)
-        ev[2].record(stream)
-        R.resa_sparse_decode(r.cache, q, r.idx, r.count, r.n_cap, r.out, r.ws, r.scale)
-        ev[3].record(stream)
-        rev = None
-        if t in rect_in:
-            rev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            rev[0].record(stream)
-            r.rectify(t, *rect_in[t])
-            rev[1].record(stream)
-        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        step_calls(t, ev)
+        evs.append((t, ev))
+    torch.cuda.synchronize()
+    times = {"append": [], "select": [], "decode": [], "rectify": []}
+    for t, ev in evs:
         times["append"].append(ev[0].elapsed_time(ev[1]))
         times["select"].append(ev[1].elapsed_time(ev[2]))
         times["decode"].append(ev[2].elapsed_time(ev[3]))
-        if rev is not None:
-            times["rectify"].append(rev[0].elapsed_time(rev[1]))
+        if t in rect_in:
+            times["rectify"].append(ev[4].elapsed_time(ev[5]))
     stage_us = {k: (1e3 * sum(v) / len(v) if v else None) for k, v in times.items()}
+    dec_ms = stage_us["decode"] * 1e-3
+    sel_ms = stage_us["select"] * 1e-3
 
     # ---- algorithmic work at the middle of the timed region ----
     tm = Wu + K // 2
@@ -278,9 +306,9 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "prefill": w.prefill_lens[0], "q_heads": w.num_q_heads,
                    "kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block": 16, "r": w.r, "n_min": w.n_min,
                    "n_local": w.n_local, "f": w.f, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "resa_sparse_decode (k_decode_split + k_decode_combine)",
+        "roofline": {"bound": "hbm", "kernel": "resa_sparse_decode (k_decode + k_decode_combine)",
                      "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": decode_traffic(w),
                      "alg_bytes_per_launch": sb["decode"], "avg_launch_us": round(dec_ms * 1e3, 2)},
         "hbm_gbs_step": round(step_alg / (ms_per_step * 1e-3) / 1e9, 1),
         "alg_bytes_per_step": int(step_alg),

@@ -430,9 +430,12 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
   }
 }
 
-// grid: x = KV head, y = sequence; 256 threads: merge a group's splits.
+// grid: x = KV head, y = sequence; 256 threads: merge a group's splits. Each
+// thread owns (head, channel) outputs; the partials of up to 16 splits are
+// requested in one batch before any is used, merged with log-sum-exp weights.
 template <typename T, int D, int G>
 __global__ __launch_bounds__(kDecThreads) void k_decode_combine(DecodeArgs a, void* __restrict__ out) {
+  constexpr int BATCH = 16;
   const CacheView& c = a.c;
   const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const size_t gi = size_t(b) * c.Hkv + g;
@@ -441,15 +444,33 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_combine(DecodeArgs a, vo
     const int h = i / D, ch = i % D;
     const float* ml = a.part_ml + (gi * a.splits * G + h) * 2;  // split sp at ml[sp * G * 2]
     const float* acc = a.part_acc + (gi * a.splits * G + h) * D + ch;
-    float mx = -__builtin_inff();
-    for (int sp = 0; sp < live; ++sp) mx = fmaxf(mx, ml[sp * G * 2]);
-    float num = 0.f, den = 0.f;
-#pragma unroll 4
-    for (int sp = 0; sp < live; ++sp) {
-      const float ms = ml[sp * G * 2];
-      const float e = ms == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(ms - mx);
-      num = fmaf(e, acc[size_t(sp) * G * D], num);
-      den = fmaf(e, ml[sp * G * 2 + 1], den);
+    float mx = -__builtin_inff(), num = 0.f, den = 0.f;
+    for (int s0 = 0; s0 < live; s0 += BATCH) {
+      float mv[BATCH], lv[BATCH], av[BATCH];
+#pragma unroll
+      for (int j = 0; j < BATCH; ++j) {
+        const int sp = min(s0 + j, live - 1);
+        mv[j] = ml[sp * G * 2];
+        lv[j] = ml[sp * G * 2 + 1];
+        av[j] = acc[size_t(sp) * G * D];
+      }
+      float bm = mx;
+#pragma unroll
+      for (int j = 0; j < BATCH; ++j)
+        if (s0 + j < live) bm = fmaxf(bm, mv[j]);
+      if (bm > mx) {
+        const float r = mx == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(mx - bm);
+        num *= r;
+        den *= r;
+        mx = bm;
+      }
+#pragma unroll
+      for (int j = 0; j < BATCH; ++j) {
+        if (s0 + j >= live) continue;
+        const float e = mv[j] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(mv[j] - mx);
+        num = fmaf(e, av[j], num);
+        den = fmaf(e, lv[j], den);
+      }
     }
     store_out<T>(out, (size_t(b) * c.Hq + size_t(g) * G + h) * D + ch, num / den);
   }

@@ -67,12 +67,6 @@ struct Chunk8<float> {
   }
 };
 
-template <typename T>
-__device__ __forceinline__ float load_q(const void* q, size_t i) {
-  if constexpr (sizeof(T) == 2) return bf16_to_f32(static_cast<const uint16_t*>(q)[i]);
-  else return static_cast<const float*>(q)[i];
-}
-
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double x) {
   const uint64_t u = uint64_t(__double_as_longlong(x));
@@ -107,8 +101,14 @@ __global__ __launch_bounds__(kScoreThreads) void k_score(CacheView c, const void
   const size_t gi = size_t(b) * c.Hkv + g;
   const int sub = lane % LPB, slot = lane / LPB, c0 = sub * 8;
 
-  // All page ids, then all descriptor loads, are issued unconditionally (blocks
+  // The group's G query rows (this lane's 8 channels) first, then all page
+  // ids, then all descriptor loads, every one issued unconditionally (blocks
   // past the sequence end re-read block 0) so they are in flight together.
+  Chunk8<T> qh[8];
+  const size_t qbase = (size_t(b) * c.Hq + size_t(g) * c.G) * D + c0;
+#pragma unroll
+  for (int h = 0; h < 8; ++h)
+    if (h < c.G) qh[h].load(q, qbase + size_t(h) * D);
   int jr[ROWS], page[ROWS];
   Chunk8<T> lo[ROWS], hi[ROWS];
 #pragma unroll
@@ -122,17 +122,17 @@ __global__ __launch_bounds__(kScoreThreads) void k_score(CacheView c, const void
     lo[r].load(c.desc, rec + c0);
     hi[r].load(c.desc, rec + D + c0);
   }
-  // pooled query for this lane's 8 channels (overlaps the descriptor loads)
+  // pooled query: heads summed in order in float64, then divided by G (G is a
+  // power of two, so multiplying by 1/G is the same exact operation)
   double qb[8];
-  {
-    const size_t base = (size_t(b) * c.Hq + size_t(g) * c.G) * D + c0;
+  const double inv_g = 1.0 / double(c.G);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) qb[e] = double(load_q<T>(q, base + e));
-    for (int h = 1; h < c.G; ++h)
+  for (int e = 0; e < 8; ++e) {
+    double acc = double(qh[0].get(e));
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qb[e] += double(load_q<T>(q, base + size_t(h) * D + e));
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qb[e] = qb[e] / double(c.G);
+    for (int h = 1; h < 8; ++h)
+      if (h < c.G) acc += double(qh[h].get(e));
+    qb[e] = acc * inv_g;
   }
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) {
