@@ -29,11 +29,52 @@ namespace {
 struct RectArgs {
   CacheView c;
   const void* q;  // [B][f][Hq][D]
-  int f, rows, rows_pad, chunk, splits;
+  int f, rows, rows_pad, target, cap;
   float scale_log2;
-  float* part_ml;   // [B][Hkv][splits][rows_pad][2]
-  float* part_acc;  // [B][Hkv][splits][rows_pad][D]
+  int4* items;      // [cap] work items: (sequence, KV head, first key, end key)
+  int2* groups;     // [B * Hkv] (first item, item count) of every (sequence, KV head)
+  int* nitems;      // [1]
+  float* part_ml;   // [cap][rows_pad][2]
+  float* part_acc;  // [cap][rows_pad][D]
 };
+
+// Work plan of one rectification, built on the device from seq_lens: every
+// (sequence, KV head) is cut into key ranges of one common length (a multiple
+// of the key tile), chosen so that all items together make about `target`
+// workgroups, i.e. one full round over the chip whatever the mix of lengths.
+// Items of one (sequence, KV head) are consecutive. 1 workgroup.
+__global__ __launch_bounds__(256) void k_rect_plan(RectArgs a) {
+  const CacheView& c = a.c;
+  __shared__ int chunk_s;
+  if (threadIdx.x == 0) {
+    long total = 0;
+    for (int b = 0; b < c.B; ++b) total += c.seq_lens[b];
+    total *= c.Hkv;
+    long chunk = (total + a.target - 1) / a.target;
+    chunk = (chunk + kRectTileKeys - 1) / kRectTileKeys * kRectTileKeys;
+    if (chunk < 256) chunk = 256;
+    if (chunk > 16384) chunk = 16384;
+    int base = 0;
+    for (int b = 0; b < c.B; ++b) {
+      const int nb = (c.seq_lens[b] + int(chunk) - 1) / int(chunk);
+      for (int g = 0; g < c.Hkv; ++g) {
+        a.groups[b * c.Hkv + g] = make_int2(base, nb);
+        base += nb;
+      }
+    }
+    a.nitems[0] = base;
+    chunk_s = int(chunk);
+  }
+  __syncthreads();
+  const int chunk = chunk_s;
+  for (int bg = threadIdx.x; bg < c.B * c.Hkv; bg += blockDim.x) {
+    const int b = bg / c.Hkv, g = bg % c.Hkv;
+    const int2 gr = a.groups[bg];
+    const int L = c.seq_lens[b];
+    for (int sp = 0; sp < gr.y; ++sp)
+      a.items[gr.x + sp] = make_int4(b, g, sp * chunk, min(L, (sp + 1) * chunk));
+  }
+}
 
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(1))) const void* global_ptr_t;
@@ -83,8 +124,8 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-// grid: x = key chunk, y = KV head, z = sequence; NWV waves. Wave w owns query
-// rows 32w .. 32w + 31 (a wave past G * f rows only loads). NS tile stages.
+// grid: x = work item (see k_rect_plan); NWV waves. Wave w owns query rows
+// 32w .. 32w + 31 (a wave past G * f rows only loads). NS tile stages.
 template <int D, int NWV, int NS>
 __global__ __launch_bounds__(64 * NWV, 2) void k_rect_mfma(RectArgs a) {
   constexpr int NT = 64 * NWV;
@@ -101,12 +142,12 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_rect_mfma(RectArgs a) {
   RESA_STAGE_DECL(4); RESA_STAGE_DECL(5); RESA_STAGE_DECL(6); RESA_STAGE_DECL(7);
   __shared__ int pages[kMaxChunkPages];
   const CacheView& c = a.c;
-  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int item = blockIdx.x;
+  if (item >= a.nitems[0]) return;
+  const int4 it = a.items[item];
+  const int b = it.x, g = it.y, key_lo = it.z, key_hi = it.w;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int L = c.seq_lens[b];
-  const int key_lo = s * a.chunk;
-  if (key_lo >= L) return;
-  const int key_hi = min(L, key_lo + a.chunk);
   const int ntiles = (key_hi - key_lo + kRectTileKeys - 1) / kRectTileKeys;
   const int G = c.G;
   const int col = lane & 31, half = lane >> 5;
@@ -294,7 +335,7 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_rect_mfma(RectArgs a) {
   if (!has_rows) return;
   const int r = wave * 32 + col;
   const float ltot = lsum + __shfl_xor(lsum, 32, 64);
-  const size_t slot = ((size_t(b) * c.Hkv + g) * a.splits + s) * a.rows_pad + r;
+  const size_t slot = size_t(item) * a.rows_pad + r;
   if (half == 0) {
     a.part_ml[slot * 2 + 0] = m;
     a.part_ml[slot * 2 + 1] = ltot;
@@ -329,18 +370,17 @@ __global__ __launch_bounds__(256) void k_rect_combine(RectArgs a, void* __restri
   const int b = blockIdx.z, g = blockIdx.y, lane = threadIdx.x & 63;
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= a.rows) return;
-  const int L = c.seq_lens[b];
-  const int live = (L + a.chunk - 1) / a.chunk;
-  const size_t base = (size_t(b) * c.Hkv + g) * a.splits;
+  const int2 gr = a.groups[size_t(b) * c.Hkv + g];
+  const int live = gr.y;
   float mx = -__builtin_inff();
-  for (int s = lane; s < live; s += 64) mx = fmaxf(mx, a.part_ml[((base + s) * a.rows_pad + r) * 2]);
+  for (int sp = lane; sp < live; sp += 64) mx = fmaxf(mx, a.part_ml[((size_t(gr.x) + sp) * a.rows_pad + r) * 2]);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
   float num[D / 64], den = 0.f;
 #pragma unroll
   for (int e = 0; e < D / 64; ++e) num[e] = 0.f;
-  for (int s = 0; s < live; ++s) {
-    const size_t slot = (base + s) * a.rows_pad + r;
+  for (int sp = 0; sp < live; ++sp) {
+    const size_t slot = (size_t(gr.x) + sp) * a.rows_pad + r;
     const float ms = a.part_ml[slot * 2];
     const float w = ms == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(ms - mx);
     den = fmaf(w, a.part_ml[slot * 2 + 1], den);
@@ -414,16 +454,17 @@ __global__ __launch_bounds__(64) void k_rect_valu(RectArgs a, void* __restrict__
 
 template <int D, int NWV, int NS>
 hipError_t launch_mfma_t(const RectArgs& a, hipStream_t st) {
-  const CacheView& c = a.c;
-  dim3 grid(a.splits, c.Hkv, c.B);
-  hipLaunchKernelGGL((k_rect_mfma<D, NWV, NS>), grid, dim3(64 * NWV), 0, st, a);
+  hipLaunchKernelGGL((k_rect_mfma<D, NWV, NS>), dim3(a.cap), dim3(64 * NWV), 0, st, a);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_mfma(const RectArgs& a, void* out, hipStream_t st) {
   const CacheView& c = a.c;
-  hipError_t e = a.rows_pad <= 128 ? launch_mfma_t<D, 4, 4>(a, st) : launch_mfma_t<D, 8, 8>(a, st);
+  hipLaunchKernelGGL(k_rect_plan, dim3(1), dim3(256), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = a.rows_pad <= 128 ? launch_mfma_t<D, 4, 4>(a, st) : launch_mfma_t<D, 8, 8>(a, st);
   if (e != hipSuccess) return e;
   dim3 g2((a.rows + 3) / 4, c.Hkv, c.B);
   hipLaunchKernelGGL((k_rect_combine<uint16_t, D>), g2, dim3(256), 0, st, a, out);
@@ -436,21 +477,24 @@ RectPlan plan_rectify(const CacheView& c, int f) {
   RectPlan p;
   p.rows = c.G * f;
   p.rows_pad = (p.rows + 31) / 32 * 32;
-  // ~1536 workgroups over the longest sequence; chunks are whole key tiles.
-  const long keys = long(c.B) * c.Hkv * c.max_seq_len;
-  long chunk = (keys + 1535) / 1536;
-  chunk = (chunk + 255) / 256 * 256;
-  if (chunk < 256) chunk = 256;
-  if (chunk > 16384) chunk = 16384;  // = kMaxChunkPages pages
-  p.chunk = int(chunk);
-  p.splits = (c.max_seq_len + p.chunk - 1) / p.chunk;
+  // one round of workgroups: two per CU with 4 waves (128 rows), one with 8
+  p.target = p.rows_pad <= 128 ? 512 : 256;
+  // items <= total / chunk + one per (sequence, KV head) while the chunk is not
+  // clamped; a clamped chunk (16384 keys) gives at most ceil(L / 16384) each
+  const int groups = c.B * c.Hkv;
+  const int clamped = groups * ((c.max_seq_len + 16383) / 16384);
+  p.cap = p.target + groups > clamped ? p.target + groups : clamped;
   return p;
+}
+
+static size_t plan_bytes(const CacheView& c, const RectPlan& p) {
+  return align_up(size_t(p.cap) * sizeof(int4), 256) + align_up(size_t(c.B) * c.Hkv * sizeof(int2), 256) + 256;
 }
 
 size_t rectify_ws_bytes(const CacheView& c, int f) {
   const RectPlan p = plan_rectify(c, f);
-  const size_t slots = size_t(c.B) * c.Hkv * p.splits * p.rows_pad;
-  return align_up(slots * 2 * sizeof(float), 256) + slots * c.D * sizeof(float);
+  const size_t slots = size_t(p.cap) * p.rows_pad;
+  return plan_bytes(c, p) + align_up(slots * 2 * sizeof(float), 256) + slots * c.D * sizeof(float);
 }
 
 hipError_t launch_rectify_attention(const CacheView& c, const void* q, int f, float scale, void* out,
@@ -462,13 +506,19 @@ hipError_t launch_rectify_attention(const CacheView& c, const void* q, int f, fl
   a.f = f;
   a.rows = p.rows;
   a.rows_pad = p.rows_pad;
-  a.chunk = p.chunk;
-  a.splits = p.splits;
+  a.target = p.target;
+  a.cap = p.cap;
   a.scale_log2 = scale * 1.4426950408889634f;
-  const size_t slots = size_t(c.B) * c.Hkv * p.splits * p.rows_pad;
-  char* scratch = static_cast<char*>(ws);
-  a.part_ml = reinterpret_cast<float*>(scratch);
-  a.part_acc = reinterpret_cast<float*>(scratch + align_up(slots * 2 * sizeof(float), 256));
+  char* w = static_cast<char*>(ws);
+  a.items = reinterpret_cast<int4*>(w);
+  w += align_up(size_t(p.cap) * sizeof(int4), 256);
+  a.groups = reinterpret_cast<int2*>(w);
+  w += align_up(size_t(c.B) * c.Hkv * sizeof(int2), 256);
+  a.nitems = reinterpret_cast<int*>(w);
+  w += 256;
+  const size_t slots = size_t(p.cap) * p.rows_pad;
+  a.part_ml = reinterpret_cast<float*>(w);
+  a.part_acc = reinterpret_cast<float*>(w + align_up(slots * 2 * sizeof(float), 256));
   if (c.dtype == RESA_BF16) return c.D == 128 ? launch_mfma<128>(a, out, st) : launch_mfma<64>(a, out, st);
   dim3 grid(c.Hq, f, c.B);
   if (c.D == 128)

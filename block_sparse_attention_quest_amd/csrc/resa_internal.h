@@ -92,8 +92,8 @@ hipError_t launch_decode(const CacheView& c, const void* q, const int32_t* idx, 
 struct RectPlan {
   int rows;     // G * f query rows per KV head
   int rows_pad; // rounded up to the row tile
-  int chunk;    // keys per split
-  int splits;   // splits per (sequence, KV head)
+  int target;   // work items aimed for (one round of workgroups)
+  int cap;      // upper bound on work items
 };
 RectPlan plan_rectify(const CacheView& c, int f);
 size_t rectify_ws_bytes(const CacheView& c, int f);
