@@ -34,7 +34,9 @@ MEASURE_STEPS = 64
 def _workloads():
     from block_sparse_attention_quest_amd import workloads as W
     return {"gqa_128k": W.gqa_128k, "llama8b_32k": W.llama8b_32k, "long_256k": W.long_256k,
-            "tiny_fp32": W.tiny_fp32}
+            "long_256k_r05": lambda: W.long_256k(r=0.05), "long_256k_f64": lambda: W.long_256k(f=64),
+            "long_256k_r05_f64": lambda: W.long_256k(r=0.05, f=64),
+            "tiny_fp32": W.tiny_fp32, "rectify_mixed": W.rectify_mixed}
 
 
 # ---------------------------------------------------------------------------
@@ -161,6 +163,47 @@ def cpu_baseline(w, first_step, budget_s):
 
 # ---------------------------------------------------------------------------
 
+def rectify_only(w, args):
+    """Rectify-only workload (mixed lengths, f new tokens per sequence): one
+    rectification event is the unit; the same event is repeated (it rewrites
+    the same positions, so every repetition does identical work)."""
+    import torch
+    from block_sparse_attention_quest_amd.schedule import ResaRunner
+
+    K, Wu = args.steps, args.warmup
+    r = ResaRunner(w)
+    r.fill_prefill()
+    r.build_descriptors()
+    from block_sparse_attention_quest_amd import workloads as W
+    q, k, v = (x.cuda() for x in W.rectify_only_inputs(w))
+    for _ in range(Wu):
+        r.rectify(0, q, k, v)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(K):
+        r.rectify(0, q, k, v)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
+    L_list = [L + w.f for L in w.prefill_lens]
+    kv, flops = rectify_work(w, L_list, w.f)
+    tflops = flops / (ms * 1e-3) / 1e12
+    gbs = kv / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "dense rectification events/s (mixed-length batch, MFMA path)", "value": round(1e3 / ms, 2),
+        "unit": "events/s", "n_gpus": 1, "steps": K, "warmup": Wu, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "f": w.f, "q_heads": w.num_q_heads,
+                   "kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "total_tokens": sum(L_list)},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "flops_per_launch": flops, "kv_bytes_per_launch": kv},
+        "cpu_baseline": None}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -185,6 +228,8 @@ def main():
     torch.cuda.set_device(0)
     K, Wu = args.steps, args.warmup
     base = _workloads()[args.workload]()
+    if base.steps == 0:
+        return rectify_only(base, args)
     w = base.replace(steps=Wu + K + MEASURE_STEPS)
     t_setup = time.perf_counter()
     print(f"[bench] setting up {w.name}: batch {w.batch}, prefill {w.prefill_lens[0]}, steps {w.steps}",

@@ -6,17 +6,22 @@
 //
 // bf16 path (k_rect_mfma): per KV head the G * f query rows form one dense
 // contraction against every key, so it runs on the matrix cores
-// (v_mfma_f32_32x32x16_bf16). One workgroup of 4 waves takes one (sequence, KV
-// head, key chunk); the K/V of the chunk are fetched once per group from HBM
-// into LDS in tiles of 32 keys and shared by all G * f rows (so HBM traffic is
-// the cache once per event, not once per head). Each wave owns 32-row tiles of
-// queries, kept in registers. Scores are computed transposed, S^T = K Q^T, so a
-// lane holds 16 keys of one query row: the softmax row max needs one cross-lane
-// step, and the probabilities feed the second product O^T = V^T P^T as its B
-// operand with no data movement (the key order inside a 16-key step is the same
-// permutation on both operands). V pages are channel-major in HBM, so the V^T
-// tile for the A operand is copied into LDS with plain 16-byte stores. Partial (m, l, O) per row and chunk go to the workspace; a combine
-// kernel merges the chunks with log-sum-exp weights.
+// (v_mfma_f32_32x32x16_bf16). The keys of all (sequence, KV head) pairs, laid
+// end to end in tiles of 32, are cut into one equal range per workgroup (the
+// work plan, k_rect_plan), so a mixed-length batch still fills the chip evenly;
+// a range that crosses from one (sequence, KV head) into the next becomes two
+// work items with a partial each. For an item the K/V tiles stream from HBM
+// into LDS once and serve all G * f rows (HBM traffic is the cache once per
+// event, not once per head). Each wave owns a 32-row tile of queries, kept in
+// registers. Scores are computed transposed, S^T = K Q^T, so a lane holds 16
+// keys of one query row and the probabilities feed O^T = V^T P^T as its B
+// operand with no data movement. The rows of a K tile are stored in LDS in an
+// order (bits 2 and 3 of the key index swapped) that makes the 8 keys a lane
+// holds per 16-key step consecutive, so the V^T operand is a single 16-byte
+// piece of the channel-major V page. Scores of tile t + 1 are issued to the
+// matrix cores before the softmax of tile t, which then overlaps them. Partial
+// (m, l, O) per row and item go to the workspace; a combine kernel merges the
+// items of every (sequence, KV head) with log-sum-exp weights.
 //
 // fp32 path (k_rect_valu): one wave per (sequence, row, head), plain VALU.
 #include <type_traits>
@@ -26,64 +31,117 @@
 namespace resa {
 namespace {
 
+constexpr int kPlanThreads = 1024;
+constexpr int kMaxItemTiles = 512;  // tiles per workgroup range (16384 keys)
+
 struct RectArgs {
   CacheView c;
   const void* q;  // [B][f][Hq][D]
-  int f, rows, rows_pad, target, cap;
+  int f, rows, rows_pad;
+  int target;     // workgroups aimed for: one round over the chip
+  int slots;      // workgroups launched (>= what any plan uses)
   float scale_log2;
-  int4* items;      // [cap] work items: (sequence, KV head, first key, end key)
-  int2* groups;     // [B * Hkv] (first item, item count) of every (sequence, KV head)
-  int* nitems;      // [1]
-  float* part_ml;   // [cap][rows_pad][2]
-  float* part_acc;  // [cap][rows_pad][D]
+  int4* items;    // [slots + B * Hkv] (sequence, KV head, first key, end key)
+  int2* groups;   // [B * Hkv] (first item, item count) of every (sequence, KV head)
+  int* wg_first;  // [slots + 1] first item of every workgroup; the rest are nitems
+  float* part_ml;   // [items][rows_pad][2]
+  float* part_acc;  // [items][rows_pad][D]
 };
 
-// Work plan of one rectification, built on the device from seq_lens: every
-// (sequence, KV head) is cut into key ranges of one common length (a multiple
-// of the key tile), chosen so that all items together make about `target`
-// workgroups, i.e. one full round over the chip whatever the mix of lengths.
-// Items of one (sequence, KV head) are consecutive. 1 workgroup.
-__global__ __launch_bounds__(256) void k_rect_plan(RectArgs a) {
-  const CacheView& c = a.c;
-  __shared__ int chunk_s;
-  if (threadIdx.x == 0) {
-    long total = 0;
-    for (int b = 0; b < c.B; ++b) total += c.seq_lens[b];
-    total *= c.Hkv;
-    long chunk = (total + a.target - 1) / a.target;
-    chunk = (chunk + kRectTileKeys - 1) / kRectTileKeys * kRectTileKeys;
-    if (chunk < 256) chunk = 256;
-    if (chunk > 16384) chunk = 16384;
-    int base = 0;
-    for (int b = 0; b < c.B; ++b) {
-      const int nb = (c.seq_lens[b] + int(chunk) - 1) / int(chunk);
-      for (int g = 0; g < c.Hkv; ++g) {
-        a.groups[b * c.Hkv + g] = make_int2(base, nb);
-        base += nb;
-      }
-    }
-    a.nitems[0] = base;
-    chunk_s = int(chunk);
-  }
+__device__ __forceinline__ long long ceil_div_ll(long long x, long long y) { return (x + y - 1) / y; }
+
+// Exclusive prefix sum over the workgroup; *total gets the sum of all values.
+__device__ long long block_exclusive_scan(long long v, long long* sh, long long* total) {
+  const int tid = threadIdx.x;
+  sh[tid] = v;
   __syncthreads();
-  const int chunk = chunk_s;
-  for (int bg = threadIdx.x; bg < c.B * c.Hkv; bg += blockDim.x) {
-    const int b = bg / c.Hkv, g = bg % c.Hkv;
-    const int2 gr = a.groups[bg];
-    const int L = c.seq_lens[b];
-    for (int sp = 0; sp < gr.y; ++sp)
-      a.items[gr.x + sp] = make_int4(b, g, sp * chunk, min(L, (sp + 1) * chunk));
+  for (int o = 1; o < kPlanThreads; o <<= 1) {
+    const long long add = tid >= o ? sh[tid - o] : 0;
+    __syncthreads();
+    sh[tid] += add;
+    __syncthreads();
   }
+  const long long incl = sh[tid];
+  *total = sh[kPlanThreads - 1];
+  __syncthreads();
+  return incl - v;
+}
+
+// Work plan of one rectification, built on the device from seq_lens.
+// Segment s = (sequence b, KV head g) covers T_b = ceil(L_b / 32) key tiles;
+// segments in order (b, then g) make one line of TT tiles, split into P equal
+// workgroup ranges at lo(w) = floor(w TT / P). P is the target, raised so that
+// no range exceeds kMaxItemTiles, and at most TT. Items are the pieces of the
+// line cut at segment starts and range starts, in line order; the item that
+// starts a range is that workgroup's first. Boundaries inside segment [a, e)
+// are lo(w) for w in [ceil((a+1) P / TT), ceil(e P / TT) - 1].
+__device__ __forceinline__ void inner_bounds(long long as, long long es, long long P, long long TT, long long* wl,
+                                             long long* wh) {
+  *wl = ceil_div_ll((as + 1) * P, TT);
+  *wh = ceil_div_ll(es * P, TT) - 1;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void k_rect_plan(RectArgs a) {
+  const CacheView& c = a.c;
+  __shared__ long long sh[kPlanThreads];
+  const int tid = threadIdx.x;
+  const int per = (c.B + kPlanThreads - 1) / kPlanThreads;
+  const int b0 = min(c.B, tid * per), b1 = min(c.B, b0 + per);
+  long long tloc = 0;
+  for (int b = b0; b < b1; ++b) tloc += (c.seq_lens[b] + kRectTileKeys - 1) / kRectTileKeys;
+  long long tsum;
+  const long long pt0 = block_exclusive_scan(tloc, sh, &tsum);
+  const long long TT = tsum * c.Hkv;
+  long long P = ceil_div_ll(TT, kMaxItemTiles);
+  if (P < a.target) P = a.target;
+  if (P > TT) P = TT;
+  const long long Hkv = c.Hkv;
+  long long cloc = 0;
+  {
+    long long pt = pt0;
+    for (int b = b0; b < b1; ++b) {
+      const long long T = (c.seq_lens[b] + kRectTileKeys - 1) / kRectTileKeys;
+      for (int g = 0; g < c.Hkv; ++g) {
+        const long long as = pt * Hkv + g * T;
+        long long wl, wh;
+        inner_bounds(as, as + T, P, TT, &wl, &wh);
+        cloc += 1 + (wh >= wl ? wh - wl + 1 : 0);
+      }
+      pt += T;
+    }
+  }
+  long long nitems;
+  long long fi = block_exclusive_scan(cloc, sh, &nitems);
+  {
+    long long pt = pt0;
+    for (int b = b0; b < b1; ++b) {
+      const int L = c.seq_lens[b];
+      const long long T = (L + kRectTileKeys - 1) / kRectTileKeys;
+      for (int g = 0; g < c.Hkv; ++g) {
+        const long long as = pt * Hkv + g * T, es = as + T;
+        long long wl, wh;
+        inner_bounds(as, es, P, TT, &wl, &wh);
+        const int cnt = 1 + int(wh >= wl ? wh - wl + 1 : 0);
+        a.groups[b * c.Hkv + g] = make_int2(int(fi), cnt);
+        for (int j = 0; j < cnt; ++j) {
+          const long long st = j == 0 ? as : (wl + j - 1) * TT / P;
+          const long long en = j == cnt - 1 ? es : (wl + j) * TT / P;
+          a.items[fi + j] = make_int4(b, g, int((st - as) * kRectTileKeys),
+                                      int(min((long long)L, (en - as) * kRectTileKeys)));
+          if (j > 0) a.wg_first[wl + j - 1] = int(fi + j);
+          else if ((wl - 1) * TT / P == as) a.wg_first[wl - 1] = int(fi);
+        }
+        fi += cnt;
+      }
+      pt += T;
+    }
+  }
+  for (long long w = P + tid; w <= a.slots; w += kPlanThreads) a.wg_first[w] = int(nitems);
 }
 
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(1))) const void* global_ptr_t;
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-// A 16-byte zero piece: the source of every tile piece that lies past the end of
-// the keys, so that such LDS slots hold zeros rather than whatever the cache
-// slot holds.
-__device__ uint4 kZeroPiece[1];
 
 // Wait until at most N vector-memory instructions of this wave are in flight.
 template <int N>
@@ -91,18 +149,21 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt(((N >> 4) & 3) << 14 | (0xF << 8) | (7 << 4) | (N & 15));
 }
 
-constexpr int kMaxChunkPages = 1024;  // keys per split <= 16384
+// Wait until this wave's LDS accesses are done.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt((3 << 14) | (7 << 4) | 15); }
 
 // Tile stages live in separate LDS arrays, one per stage, and the tile loop is
 // unrolled by the stage count, so every access names one array at compile time.
 // The compiler can then tell that reading one stage does not depend on the
 // direct-to-LDS loads still in flight into the others.
-//   K stage: [32 keys][D/8 pieces of 8 channels]; piece c of key r sits at
-//            position c ^ (r % (D/8)) of its row (XOR swizzle: the 32 rows read
-//            at one column by an MFMA operand load hit distinct banks).
-//   V stage: [4 groups of 8 keys][D channels] pieces; piece (q, ch) holds channel
+// A stage array holds the K tile, then the V tile:
+//   K tile: [32 rows][D/8 pieces of 8 channels]. Row i holds key pi(i), pi
+//            swapping bits 2 and 3 of the index; piece c of a row sits at
+//            position c ^ (i % (D/8)) (XOR swizzle: the 32 rows read at one
+//            column by an MFMA operand load hit distinct banks).
+//   V tile: [4 groups of 8 keys][D channels] pieces; piece (q, ch) holds channel
 //            ch of keys 8q .. 8q + 7 (V page tiles are channel-major in HBM).
-#define RESA_STAGE_DECL(i) __shared__ uint4 sk##i[PIECES], sv##i[PIECES]
+#define RESA_STAGE_DECL(i) __shared__ uint4 st##i[2 * PIECES]
 template <int S>
 __device__ __forceinline__ uint4* pick(uint4* a0, uint4* a1, uint4* a2, uint4* a3, uint4* a4, uint4* a5,
                                        uint4* a6, uint4* a7) {
@@ -124,8 +185,8 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-// grid: x = work item (see k_rect_plan); NWV waves. Wave w owns query rows
-// 32w .. 32w + 31 (a wave past G * f rows only loads). NS tile stages.
+// grid: x = workgroup range of the plan (slots); NWV waves. Wave w owns query
+// rows 32w .. 32w + 31 (a wave past G * f rows only loads). NS tile stages.
 template <int D, int NWV, int NS>
 __global__ __launch_bounds__(64 * NWV, 2) void k_rect_mfma(RectArgs a) {
   constexpr int NT = 64 * NWV;
@@ -135,218 +196,282 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_rect_mfma(RectArgs a) {
   constexpr int PIECES = kRectTileKeys * D / 8;  // per tile, K and V each
   constexpr int INSTR = 2 * PIECES / 64;         // wave-wide loads per tile
   constexpr int LPT = INSTR / NWV;               // loads per thread per tile
-  static_assert(INSTR % NWV == 0, "tile loads must split evenly over the waves");
-  static_assert(NS >= 2 && NS <= 8, "2 .. 8 stages");
+  constexpr int PAGE_BYTES = kBlock * D * 2;     // one KV head's K (or V) of a page
+  static_assert(INSTR % NWV == 0 && (INSTR / NWV) % 2 == 0 || INSTR / NWV == 1,
+                "tile loads must split evenly over the waves");
+  static_assert(NS >= 4 && NS <= 8 && NS % 2 == 0, "4, 6 or 8 stages");
   constexpr float kLazy = 8.0f;    // log2 units
   RESA_STAGE_DECL(0); RESA_STAGE_DECL(1); RESA_STAGE_DECL(2); RESA_STAGE_DECL(3);
   RESA_STAGE_DECL(4); RESA_STAGE_DECL(5); RESA_STAGE_DECL(6); RESA_STAGE_DECL(7);
-  __shared__ int pages[kMaxChunkPages];
+  __shared__ int pages[2 * (kMaxItemTiles + 2 * NS)];
   const CacheView& c = a.c;
-  const int item = blockIdx.x;
-  if (item >= a.nitems[0]) return;
-  const int4 it = a.items[item];
-  const int b = it.x, g = it.y, key_lo = it.z, key_hi = it.w;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int L = c.seq_lens[b];
-  const int ntiles = (key_hi - key_lo + kRectTileKeys - 1) / kRectTileKeys;
-  const int G = c.G;
   const int col = lane & 31, half = lane >> 5;
+  const int G = c.G;
   const bool has_rows = wave * 32 < a.rows;  // wave-uniform
-  const int first_masked = L - a.f;          // keys from here on are seen by some rows only
+  const int item_begin = a.wg_first[blockIdx.x], item_end = a.wg_first[blockIdx.x + 1];
 
-  // page ids of the chunk
-  const int page0 = key_lo >> 4;
-  const int npages = (key_hi - 1) / kBlock - page0 + 1;
-  for (int i = tid; i < npages; i += NT) pages[i] = c.bt[size_t(b) * c.maxb + page0 + i];
-
-  // this lane's query row as MFMA B operands (S^T = K Q^T)
-  bf16x8_t qreg[KSTEPS];
-  int limit;  // last key position the row may see (-1: padding row)
-  {
-    const int r = wave * 32 + col;
-    const bool live = r < a.rows;
-    const int i = r / G, h = r % G;
-    limit = live ? L - a.f + i : -1;
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
-                           ((size_t(b) * a.f + (live ? i : 0)) * c.Hq + size_t(g) * G + (live ? h : 0)) * D;
-    // a padding row reads row 0: all of its keys are masked and it writes nothing
+  // Per-thread constants of the tile loads. Load li of a tile is one
+  // wave-wide instruction; with two or more per thread the first half fill
+  // the K stage and the rest the V stage, with one per thread the first half
+  // of the waves take K.
+  int ld_off[LPT];   // byte offset inside the page's K or V tile
+  int ld_ph[LPT];    // which of the tile's two pages
+  int ld_dst[LPT];   // first piece of the instruction in its stage array (wave-uniform)
+  bool ld_k[LPT];    // wave-uniform; compile-time when LPT >= 2
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks)
-      qreg[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qrow + ks * 16 + 8 * half));
-  }
-  wait_vmcnt<0>();  // query rows and page ids are in before any tile load is issued
-  __syncthreads();  // page ids visible
-
-  const uint16_t* kb = static_cast<const uint16_t*>(c.k);
-  const uint16_t* vb = static_cast<const uint16_t*>(c.v);
-  // Issue the LPT direct-to-LDS loads of tile ti into the given stage arrays.
-  auto issue_tile = [&](int ti, uint4* kst, uint4* vst) {
-    const int base = key_lo + ti * kRectTileKeys;
-#pragma unroll
-    for (int li = 0; li < LPT; ++li) {
-      const int ins = li * NWV + wave;  // wave-uniform
-      const void* src;
-      uint4* dst;
-      if (ins < INSTR / 2) {  // K pieces
-        const int pidx = ins * 64 + lane;
-        const int key = pidx / CPR, cpos = pidx % CPR;
-        const int cl = cpos ^ (key % CPR);
-        const int kg = base + key;
-        src = kg < key_hi ? static_cast<const void*>(
-                                kb + ((size_t(pages[(kg >> 4) - page0]) * c.Hkv + g) * kBlock + (kg & 15)) * D + cl * 8)
-                          : static_cast<const void*>(kZeroPiece);
-        dst = kst + ins * 64;
-      } else {  // V pieces
-        const int pidx = (ins - INSTR / 2) * 64 + lane;
-        const int q = pidx / D, ch = pidx % D;
-        const int t0 = base + 8 * q;
-        src = t0 < key_hi ? static_cast<const void*>(
-                                vb + ((size_t(pages[(t0 >> 4) - page0]) * c.Hkv + g) * D + ch) * kBlock + (t0 & 15))
-                          : static_cast<const void*>(kZeroPiece);
-        dst = vst + (ins - INSTR / 2) * 64;
-      }
-      __builtin_amdgcn_global_load_lds((global_ptr_t)src, (lds_ptr_t)dst, 16, 0, 0);
-    }
-  };
-
-  f32x16_t o[DT];
-#pragma unroll
-  for (int t = 0; t < DT; ++t)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
-  float m = -__builtin_inff(), lsum = 0.f;
-
-  auto compute = [&](int ti, const uint4* kst, const uint4* vst) {
-    const int base = key_lo + ti * kRectTileKeys;
-    f32x16_t sacc;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
-    bf16x8_t ak[KSTEPS];
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks)
-      ak[ks] = __builtin_bit_cast(bf16x8_t, kst[col * CPR + ((2 * ks + half) ^ (col % CPR))]);
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks)
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[ks], qreg[ks], sacc, 0, 0, 0);
-    // lane holds keys base + 8 (r/4) + 4 half + r%4 of query row `col`
-    float x[16];
-    if (base + kRectTileKeys > first_masked || base + kRectTileKeys > key_hi) {  // wave-uniform
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = base + 8 * (r / 4) + 4 * half + (r % 4);
-        x[r] = (key < key_hi && key <= limit) ? sacc[r] * a.scale_log2 : -__builtin_inff();
-      }
+  for (int li = 0; li < LPT; ++li) {
+    int ins;
+    if constexpr (LPT >= 2) {
+      ld_k[li] = li < LPT / 2;
+      ins = (li % (LPT / 2)) * NWV + wave;
     } else {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = limit >= 0 ? sacc[r] * a.scale_log2 : -__builtin_inff();
+      ld_k[li] = wave < NWV / 2;
+      ins = wave % (NWV / 2);
     }
-    float tmax = x[0];
+    const int pidx = ins * 64 + lane;
+    if (ld_k[li]) {
+      const int i = pidx / CPR, cp = (pidx % CPR) ^ (i % CPR);
+      const int kt = (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
+      ld_off[li] = ((kt & 15) * D + cp * 8) * 2;
+      ld_ph[li] = kt >> 4;
+    } else {
+      const int q = pidx / D, ch = pidx % D;
+      ld_off[li] = (ch * kBlock + 8 * (q & 1)) * 2;
+      ld_ph[li] = q >> 1;
+    }
+    ld_dst[li] = ins * 64;
+  }
+  const uint32_t ones = 0x3F803F80u;  // bf16 pair (1, 1)
+  // LDS byte offsets of this lane's operand pieces inside a stage: K piece of
+  // k-step ks, and the first V piece (the others are fixed strides from it)
+  uint32_t koff_base[KSTEPS];
 #pragma unroll
-    for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, x[r]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    // the running max moves only when a logit exceeds it by more than 2^8;
-    // numerator and denominator share every rescale
-    if (__builtin_amdgcn_ballot_w64(tmax > m + kLazy)) {
+  for (int ks = 0; ks < KSTEPS; ++ks) koff_base[ks] = (col * CPR + ((2 * ks + half) ^ (col % CPR))) * 16;
+  const uint32_t voff_base = (half * D + col) * 16;
+
+  for (int item = item_begin; item < item_end; ++item) {
+    const int4 it = a.items[item];
+    const int b = it.x, g = it.y, key_lo = it.z, key_hi = it.w;
+    const int L = c.seq_lens[b];
+    const int ntiles = (key_hi - key_lo + kRectTileKeys - 1) / kRectTileKeys;
+    const int first_masked = L - a.f;  // keys from here on are seen by some rows only
+
+    __syncthreads();  // the previous item is done with the page list and the stages
+    // page ids of the item's tiles (two per tile) and of the tiles requested
+    // past the end (the last page repeated)
+    const int page0 = key_lo / kBlock, last = (key_hi - 1) / kBlock;
+    const int nreq = (ntiles + NS - 1) / NS * NS + NS - 1;  // tiles the pipeline requests
+    for (int i = tid; i < 2 * nreq; i += NT) pages[i] = c.bt[size_t(b) * c.maxb + min(page0 + i, last)];
+
+    // this lane's query row as MFMA B operands (S^T = K Q^T)
+    bf16x8_t qreg[KSTEPS];
+    int limit;  // last key position the row may see (-1: padding row)
+    {
+      const int r = wave * 32 + col;
+      const bool live = r < a.rows;
+      const int i = r / G, h = r % G;
+      limit = live ? L - a.f + i : -1;
+      const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
+                             ((size_t(b) * a.f + (live ? i : 0)) * c.Hq + size_t(g) * G + (live ? h : 0)) * D;
+      // a padding row reads row 0: it writes nothing that is read back
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks)
+        qreg[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qrow + ks * 16 + 8 * half));
+    }
+    wait_vmcnt<0>();  // query rows and page ids are in before any tile load is issued
+    __syncthreads();  // page ids visible
+
+    const char* kbase = static_cast<const char*>(c.k) + size_t(g) * PAGE_BYTES;
+    const char* vbase = static_cast<const char*>(c.v) + size_t(g) * PAGE_BYTES;
+    const size_t pstride = size_t(c.Hkv) * PAGE_BYTES;
+    // Issue the LPT direct-to-LDS loads of tile ti into the given stage arrays.
+    auto issue_tile = [&](int ti, uint4* kst, uint4* vst) {
+#pragma unroll
+      for (int li = 0; li < LPT; ++li) {
+        const int page = pages[2 * ti + ld_ph[li]];
+        const bool isk = LPT >= 2 ? li < LPT / 2 : ld_k[li];
+        const char* src = (isk ? kbase : vbase) + size_t(page) * pstride + ld_off[li];
+        uint4* dst = (isk ? kst : vst) + ld_dst[li];
+        __builtin_amdgcn_global_load_lds((global_ptr_t)src, (lds_ptr_t)dst, 16, 0, 0);
+      }
+    };
+
+    f32x16_t o[DT];
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
+    float m = -__builtin_inff(), lsum = 0.f;
+
+    // S^T tile of one stage: lane holds keys 16 (r / 8) + 8 half + r % 8 of
+    // query row `col` (tile-relative key order after the row permutation).
+    // The lane offsets pass through an empty asm at every use, so the compiler
+    // adds them to each stage's base where they are read instead of keeping a
+    // precomputed address per stage and k-step live across the loop.
+    auto score = [&](f32x16_t& acc, const uint4* kst) {
+      uint32_t ko[KSTEPS];
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        ko[ks] = koff_base[ks];
+        asm volatile("" : "+v"(ko[ks]));
+      }
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const bf16x8_t ak =
+            __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(kst) + ko[ks]));
+        if (ks == 0) {
+          f32x16_t z;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) z[r] = 0.f;
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[0], z, 0, 0, 0);
+        } else {
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[ks], acc, 0, 0, 0);
+        }
+      }
+    };
+
+    auto rescale = [&](float tmax) {
       const float mnew = fmaxf(m, tmax);
-      const float alpha = m == -__builtin_inff() ? (mnew == -__builtin_inff() ? 1.f : 0.f)
-                                                 : __builtin_amdgcn_exp2f(m - mnew);
+      // m == -inf: nothing accumulated yet, o and lsum are zero
+      const float alpha = m == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m - mnew);
       lsum *= alpha;
 #pragma unroll
       for (int t = 0; t < DT; ++t) o[t] *= alpha;
       m = mnew;
-    }
-    float p[16];
+    };
+
+    auto half_max = [&](float x) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+      return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    };
+
+    // softmax of tile t and its O^T update
+    // softmax of tile t and its O^T update
+    auto consume = [&](int t, f32x16_t& sacc, const uint4* vst) {
+      const int base = key_lo + t * kRectTileKeys;
+      if (base + kRectTileKeys > first_masked || base + kRectTileKeys > key_hi) {  // wave-uniform
+        int k0 = 8 * half;
+        asm volatile("" : "+v"(k0));
+        // highest key this lane's row may see, relative to the lane's first key
+        const int vis = min(key_hi - 1, limit) - (base + k0);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      p[r] = x[r] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(x[r] - m);
-      lsum += p[r];
-    }
-    bf16x8_t pb[2];
-#pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
-      uint32_t w[4];
-#pragma unroll
-      for (int x2 = 0; x2 < 4; ++x2) {
-        const f32x2_t pr = {p[8 * k2 + 2 * x2], p[8 * k2 + 2 * x2 + 1]};
-        w[x2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2_t));
+        for (int r = 0; r < 16; ++r) sacc[r] = 16 * (r / 8) + (r % 8) <= vis ? sacc[r] : -__builtin_inff();
       }
-      pb[k2] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
-    }
+      float mx = sacc[0];
 #pragma unroll
-    for (int t = 0; t < DT; ++t) {
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
+      const float tmax = half_max(mx) * a.scale_log2;
+      // the running max moves only when a logit exceeds it by more than 2^8;
+      // numerator and denominator share every rescale
+      if (__builtin_amdgcn_ballot_w64(tmax > m + kLazy)) rescale(tmax);
+      // a row that has seen no key yet (m = -inf) has only masked logits here
+      const float nm = m == -__builtin_inff() ? 0.f : -m;
+      float p[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(sacc[r], a.scale_log2, nm));
+      bf16x8_t pb[2];
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
-        // keys 16 k2 + 4 half + [0, 4) from group 2 k2, + 8 from group 2 k2 + 1
-        const uint2 lo = reinterpret_cast<const uint2*>(&vst[(2 * k2) * D + t * 32 + col])[half];
-        const uint2 hi = reinterpret_cast<const uint2*>(&vst[(2 * k2 + 1) * D + t * 32 + col])[half];
-        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
-        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[k2], o[t], 0, 0, 0);
-      }
-    }
-  };
-
-  // Pipeline: NS - 1 tiles are in flight. At step t the wave waits for its own
-  // loads of tile t, a barrier makes everyone's visible, tile t + NS - 1 is
-  // requested into the stage tile t - 1 used (every wave finished computing it
-  // before this barrier), and tile t is computed.
-  static_for<0, NS - 1>([&](auto S) {
-    if (S.value < ntiles)
-      issue_tile(S.value, pick<S.value>(sk0, sk1, sk2, sk3, sk4, sk5, sk6, sk7),
-                 pick<S.value>(sv0, sv1, sv2, sv3, sv4, sv5, sv6, sv7));
-  });
-  for (int t0 = 0; t0 < ntiles; t0 += NS) {
-    static_for<0, NS>([&](auto S) {
-      const int t = t0 + S.value;
-      if (t >= ntiles) return;
-      constexpr int SN = (S.value + NS - 1) % NS;  // stage of tile t + NS - 1
-      uint4* kcur = pick<S.value>(sk0, sk1, sk2, sk3, sk4, sk5, sk6, sk7);
-      uint4* vcur = pick<S.value>(sv0, sv1, sv2, sv3, sv4, sv5, sv6, sv7);
-      const int ahead = min(NS - 2, ntiles - 1 - t);  // tiles after t already requested
-      if (ahead >= NS - 2) wait_vmcnt<(NS - 2) * LPT>();
-      else if (ahead <= 0) wait_vmcnt<0>();
-      else if (ahead == 1) wait_vmcnt<LPT>();
-      else if (ahead == 2) wait_vmcnt<2 * LPT>();
-      else if (ahead == 3) wait_vmcnt<3 * LPT>();
-      else if (ahead == 4) wait_vmcnt<4 * LPT>();
-      else wait_vmcnt<0>();
-      // Every wave has its own loads of tile t complete; the bare barrier (no
-      // fence) then makes the whole tile visible without draining the loads of
-      // later tiles that are still in flight. The memory clobber keeps the
-      // compiler from moving LDS accesses across it.
-      asm volatile("s_barrier" ::: "memory");
-      if (t == ntiles - 1 && (key_hi & 7) != 0) {
-        // the last V group holds keys past the end: zero them
-        const int q = ((key_hi - key_lo) - t * kRectTileKeys) / 8;
-        const int from = key_hi & 7;
-        for (int ch = tid; ch < D; ch += NT) {
-          uint16_t* e = reinterpret_cast<uint16_t*>(&vcur[q * D + ch]);
-          for (int x2 = from; x2 < 8; ++x2) e[x2] = 0;
+        uint32_t w[4];
+#pragma unroll
+        for (int x2 = 0; x2 < 4; ++x2) {
+          const f32x2_t pr = {p[8 * k2 + 2 * x2], p[8 * k2 + 2 * x2 + 1]};
+          w[x2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2_t));
+          // the denominator sums the same rounded probabilities the product uses
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[x2]),
+                                                 __builtin_bit_cast(bf16x2_t, ones), lsum, false);
         }
-        __syncthreads();
+        pb[k2] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
       }
-      if (t + NS - 1 < ntiles)
-        issue_tile(t + NS - 1, pick<SN>(sk0, sk1, sk2, sk3, sk4, sk5, sk6, sk7),
-                   pick<SN>(sv0, sv1, sv2, sv3, sv4, sv5, sv6, sv7));
-      if (has_rows) compute(t, kcur, vcur);
-    });
-  }
+      const uint4* vl = vst + (half * D + col);
+#pragma unroll
+      for (int tt = 0; tt < DT; ++tt)
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          // keys 16 k2 + 8 half + [0, 8): one piece of channel 32 tt + col
+          const uint4 vv = vl[2 * k2 * D + tt * 32];
+          o[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vv), pb[k2], o[tt], 0, 0, 0);
+        }
+    };
 
-  // partials: lane holds O^T[dcol][row col] for dcol = 32t + 8(r/4) + 4 half + r%4
-  if (!has_rows) return;
-  const int r = wave * 32 + col;
-  const float ltot = lsum + __shfl_xor(lsum, 32, 64);
-  const size_t slot = size_t(item) * a.rows_pad + r;
-  if (half == 0) {
-    a.part_ml[slot * 2 + 0] = m;
-    a.part_ml[slot * 2 + 1] = ltot;
+    // Pipeline: NS - 1 tiles are requested ahead. At step t the wave waits for
+    // its own loads of tile t + 1, a barrier makes everyone's visible, tile
+    // t + NS - 1 is requested into the stage tile t - 1 used (every wave
+    // finished tile t - 1 before this barrier), the scores of tile t + 1 go to
+    // the matrix cores and tile t (scored one step earlier) is consumed. Every
+    // step requests a tile, past the end one of the repeated last page (its
+    // contents are never used), so each wait is a fixed count and the
+    // compiler's own tracking of the loads sees every stage complete before it
+    // is read, without adding waits of its own.
+    f32x16_t s0, s1;
+    static_for<0, NS - 1>([&](auto S) {
+      issue_tile(S.value, pick<S.value>(st0, st1, st2, st3, st4, st5, st6, st7),
+                 pick<S.value>(st0, st1, st2, st3, st4, st5, st6, st7) + PIECES);
+    });
+    wait_vmcnt<(NS - 2) * LPT>();
+    asm volatile("s_barrier" ::: "memory");
+    if (has_rows) score(s0, st0);
+    for (int t0 = 0; t0 < ntiles; t0 += NS) {
+      static_for<0, NS>([&](auto S) {
+        const int t = t0 + S.value;
+        constexpr int SN = (S.value + 1) % NS;       // stage of tile t + 1
+        constexpr int SR = (S.value + NS - 1) % NS;  // stage of tile t + NS - 1
+        // tiles t + 2 .. t + NS - 2 may stay in flight
+        wait_vmcnt<(NS - 3) * LPT>();
+        // Every wave has its own loads of tile t + 1 complete; the bare barrier
+        // (no fence) then makes the whole tile visible without draining the
+        // loads of later tiles that are still in flight. The memory clobber
+        // keeps the compiler from moving LDS accesses across it.
+        asm volatile("s_barrier" ::: "memory");
+        const int kk = key_hi - (key_lo + t * kRectTileKeys);  // keys of tile t
+        if (kk > 0 && kk < kRectTileKeys) {  // workgroup-uniform: the last tile is partial
+          // its V slots past the end may hold anything (p is 0 there, but
+          // 0 * NaN is not): zero them
+          uint4* vz = pick<S.value>(st0, st1, st2, st3, st4, st5, st6, st7) + PIECES;
+          for (int idx = tid; idx < 4 * D; idx += NT) {
+            const int from = kk - 8 * (idx / D);  // valid keys in this piece
+            if (from < 8) {
+              uint16_t* e = reinterpret_cast<uint16_t*>(&vz[idx]);
+              for (int x2 = from < 0 ? 0 : from; x2 < 8; ++x2) e[x2] = 0;
+            }
+          }
+          wait_lgkm0();
+          asm volatile("s_barrier" ::: "memory");
+        }
+        issue_tile(t + NS - 1, pick<SR>(st0, st1, st2, st3, st4, st5, st6, st7),
+                   pick<SR>(st0, st1, st2, st3, st4, st5, st6, st7) + PIECES);
+        if (has_rows) {
+          if constexpr (S.value % 2 == 0) {
+            if (t + 1 < ntiles) score(s1, pick<SN>(st0, st1, st2, st3, st4, st5, st6, st7));
+            if (t < ntiles) consume(t, s0, pick<S.value>(st0, st1, st2, st3, st4, st5, st6, st7) + PIECES);
+          } else {
+            if (t + 1 < ntiles) score(s0, pick<SN>(st0, st1, st2, st3, st4, st5, st6, st7));
+            if (t < ntiles) consume(t, s1, pick<S.value>(st0, st1, st2, st3, st4, st5, st6, st7) + PIECES);
+          }
+        }
+      });
+    }
+    wait_vmcnt<0>();  // the loads past the end land before the stages are reused
+
+    // partials: lane holds O^T[dcol][row col] for dcol = 32t + 8(r/4) + 4 half + r%4
+    if (has_rows) {
+      const int r = wave * 32 + col;
+      const float ltot = lsum + __shfl_xor(lsum, 32, 64);
+      const size_t slot = size_t(item) * a.rows_pad + r;
+      if (half == 0) {
+        a.part_ml[slot * 2 + 0] = m;
+        a.part_ml[slot * 2 + 1] = ltot;
+      }
+      float* dst = a.part_acc + slot * D;
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *reinterpret_cast<float4*>(dst + t * 32 + 8 * q4 + 4 * half) =
+              make_float4(o[t][4 * q4 + 0], o[t][4 * q4 + 1], o[t][4 * q4 + 2], o[t][4 * q4 + 3]);
+    }
   }
-  float* dst = a.part_acc + slot * D;
-#pragma unroll
-  for (int t = 0; t < DT; ++t)
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4)
-      *reinterpret_cast<float4*>(dst + t * 32 + 8 * q4 + 4 * half) =
-          make_float4(o[t][4 * q4 + 0], o[t][4 * q4 + 1], o[t][4 * q4 + 2], o[t][4 * q4 + 3]);
 }
 #undef RESA_STAGE_DECL
 
@@ -454,14 +579,14 @@ __global__ __launch_bounds__(64) void k_rect_valu(RectArgs a, void* __restrict__
 
 template <int D, int NWV, int NS>
 hipError_t launch_mfma_t(const RectArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((k_rect_mfma<D, NWV, NS>), dim3(a.cap), dim3(64 * NWV), 0, st, a);
+  hipLaunchKernelGGL((k_rect_mfma<D, NWV, NS>), dim3(a.slots), dim3(64 * NWV), 0, st, a);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_mfma(const RectArgs& a, void* out, hipStream_t st) {
   const CacheView& c = a.c;
-  hipLaunchKernelGGL(k_rect_plan, dim3(1), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_rect_plan, dim3(1), dim3(kPlanThreads), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = a.rows_pad <= 128 ? launch_mfma_t<D, 4, 4>(a, st) : launch_mfma_t<D, 8, 8>(a, st);
@@ -477,18 +602,21 @@ RectPlan plan_rectify(const CacheView& c, int f) {
   RectPlan p;
   p.rows = c.G * f;
   p.rows_pad = (p.rows + 31) / 32 * 32;
-  // one round of workgroups: two per CU with 4 waves (128 rows), one with 8
+  // one round of workgroups: two per CU with 4 waves (<= 128 rows), one with 8
   p.target = p.rows_pad <= 128 ? 512 : 256;
-  // items <= total / chunk + one per (sequence, KV head) while the chunk is not
-  // clamped; a clamped chunk (16384 keys) gives at most ceil(L / 16384) each
-  const int groups = c.B * c.Hkv;
-  const int clamped = groups * ((c.max_seq_len + 16383) / 16384);
-  p.cap = p.target + groups > clamped ? p.target + groups : clamped;
+  // the plan raises the count so that no range exceeds kMaxItemTiles tiles;
+  // the launch covers the largest cache the capacities allow
+  const long long groups = (long long)c.B * c.Hkv;
+  const long long tt_max = groups * ((c.max_seq_len + kRectTileKeys - 1) / kRectTileKeys);
+  const long long need = (tt_max + kMaxItemTiles - 1) / kMaxItemTiles;
+  p.slots = int(need > p.target ? need : p.target);
+  p.cap = p.slots + int(groups);  // items: one per range plus one per (sequence, KV head)
   return p;
 }
 
 static size_t plan_bytes(const CacheView& c, const RectPlan& p) {
-  return align_up(size_t(p.cap) * sizeof(int4), 256) + align_up(size_t(c.B) * c.Hkv * sizeof(int2), 256) + 256;
+  return align_up(size_t(p.cap) * sizeof(int4), 256) + align_up(size_t(c.B) * c.Hkv * sizeof(int2), 256) +
+         align_up(size_t(p.slots + 1) * sizeof(int), 256);
 }
 
 size_t rectify_ws_bytes(const CacheView& c, int f) {
@@ -507,15 +635,15 @@ hipError_t launch_rectify_attention(const CacheView& c, const void* q, int f, fl
   a.rows = p.rows;
   a.rows_pad = p.rows_pad;
   a.target = p.target;
-  a.cap = p.cap;
+  a.slots = p.slots;
   a.scale_log2 = scale * 1.4426950408889634f;
   char* w = static_cast<char*>(ws);
   a.items = reinterpret_cast<int4*>(w);
   w += align_up(size_t(p.cap) * sizeof(int4), 256);
   a.groups = reinterpret_cast<int2*>(w);
   w += align_up(size_t(c.B) * c.Hkv * sizeof(int2), 256);
-  a.nitems = reinterpret_cast<int*>(w);
-  w += 256;
+  a.wg_first = reinterpret_cast<int*>(w);
+  w += align_up(size_t(p.slots + 1) * sizeof(int), 256);
   const size_t slots = size_t(p.cap) * p.rows_pad;
   a.part_ml = reinterpret_cast<float*>(w);
   a.part_acc = reinterpret_cast<float*>(w + align_up(slots * 2 * sizeof(float), 256));

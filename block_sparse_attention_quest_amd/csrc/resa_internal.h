@@ -92,7 +92,8 @@ hipError_t launch_decode(const CacheView& c, const void* q, const int32_t* idx, 
 struct RectPlan {
   int rows;     // G * f query rows per KV head
   int rows_pad; // rounded up to the row tile
-  int target;   // work items aimed for (one round of workgroups)
+  int target;   // workgroups aimed for (one round over the chip)
+  int slots;    // workgroups launched: the most any plan within the capacities uses
   int cap;      // upper bound on work items
 };
 RectPlan plan_rectify(const CacheView& c, int f);
