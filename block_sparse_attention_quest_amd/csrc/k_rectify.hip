@@ -44,27 +44,35 @@ struct RectArgs {
   int4* items;    // [slots + B * Hkv] (sequence, KV head, first key, end key)
   int2* groups;   // [B * Hkv] (first item, item count) of every (sequence, KV head)
   int* wg_first;  // [slots + 1] first item of every workgroup; the rest are nitems
+  long long* ptile;  // [B] key tiles of the sequences before each one
   float* part_ml;   // [items][rows_pad][2]
   float* part_acc;  // [items][rows_pad][D]
 };
 
 __device__ __forceinline__ long long ceil_div_ll(long long x, long long y) { return (x + y - 1) / y; }
 
-// Exclusive prefix sum over the workgroup; *total gets the sum of all values.
+// Exclusive prefix sum over the workgroup (wave shuffles, then one pass over
+// the wave totals); *total gets the sum of all values.
 __device__ long long block_exclusive_scan(long long v, long long* sh, long long* total) {
-  const int tid = threadIdx.x;
-  sh[tid] = v;
-  __syncthreads();
-  for (int o = 1; o < kPlanThreads; o <<= 1) {
-    const long long add = tid >= o ? sh[tid - o] : 0;
-    __syncthreads();
-    sh[tid] += add;
-    __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  long long x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const long long y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
   }
-  const long long incl = sh[tid];
-  *total = sh[kPlanThreads - 1];
+  if (lane == 63) sh[wave] = x;
   __syncthreads();
-  return incl - v;
+  long long before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kPlanThreads / 64; ++w) {
+    const long long t = sh[w];
+    before += w < wave ? t : 0;
+    tot += t;
+  }
+  __syncthreads();
+  *total = tot;
+  return before + x - v;
 }
 
 // Work plan of one rectification, built on the device from seq_lens.
@@ -74,67 +82,79 @@ __device__ long long block_exclusive_scan(long long v, long long* sh, long long*
 // no range exceeds kMaxItemTiles, and at most TT. Items are the pieces of the
 // line cut at segment starts and range starts, in line order; the item that
 // starts a range is that workgroup's first. Boundaries inside segment [a, e)
-// are lo(w) for w in [ceil((a+1) P / TT), ceil(e P / TT) - 1].
-__device__ __forceinline__ void inner_bounds(long long as, long long es, long long P, long long TT, long long* wl,
-                                             long long* wh) {
-  *wl = ceil_div_ll((as + 1) * P, TT);
-  *wh = ceil_div_ll(es * P, TT) - 1;
-}
-
+// are lo(w) for w in [ceil((a+1) P / TT), ceil(e P / TT) - 1]. Threads take
+// contiguous runs of sequences, then of segments; consecutive boundaries are
+// stepped without division (lo(w) = w q + floor(w r / P), TT = q P + r).
 __global__ __launch_bounds__(kPlanThreads) void k_rect_plan(RectArgs a) {
   const CacheView& c = a.c;
-  __shared__ long long sh[kPlanThreads];
+  __shared__ long long sh[kPlanThreads / 64];
   const int tid = threadIdx.x;
-  const int per = (c.B + kPlanThreads - 1) / kPlanThreads;
-  const int b0 = min(c.B, tid * per), b1 = min(c.B, b0 + per);
+  const long long Hkv = c.Hkv;
+  auto tiles = [&](int b) { return (long long)(c.seq_lens[b] + kRectTileKeys - 1) / kRectTileKeys; };
+
+  const int per_b = (c.B + kPlanThreads - 1) / kPlanThreads;
+  const int b0 = min(c.B, tid * per_b), b1 = min(c.B, b0 + per_b);
   long long tloc = 0;
-  for (int b = b0; b < b1; ++b) tloc += (c.seq_lens[b] + kRectTileKeys - 1) / kRectTileKeys;
+  for (int b = b0; b < b1; ++b) tloc += tiles(b);
   long long tsum;
-  const long long pt0 = block_exclusive_scan(tloc, sh, &tsum);
-  const long long TT = tsum * c.Hkv;
+  long long pt = block_exclusive_scan(tloc, sh, &tsum);
+  for (int b = b0; b < b1; ++b) {
+    a.ptile[b] = pt;
+    pt += tiles(b);
+  }
+  const long long TT = tsum * Hkv;
   long long P = ceil_div_ll(TT, kMaxItemTiles);
   if (P < a.target) P = a.target;
   if (P > TT) P = TT;
-  const long long Hkv = c.Hkv;
+  const long long q = TT / P, r = TT % P;
+  __syncthreads();  // ptile visible to the workgroup
+
+  const int S = c.B * c.Hkv;
+  const int per_s = (S + kPlanThreads - 1) / kPlanThreads;
+  const int s0 = min(S, tid * per_s), s1 = min(S, s0 + per_s);
+  // segment s: first tile, end tile, and the range starts strictly inside
+  auto segment = [&](int s, long long& as, long long& es, long long& wl, long long& wh) {
+    const int b = s / c.Hkv, g = s % c.Hkv;
+    const long long T = tiles(b);
+    as = a.ptile[b] * Hkv + g * T;
+    es = as + T;
+    wl = ceil_div_ll((as + 1) * P, TT);
+    wh = ceil_div_ll(es * P, TT) - 1;
+  };
   long long cloc = 0;
-  {
-    long long pt = pt0;
-    for (int b = b0; b < b1; ++b) {
-      const long long T = (c.seq_lens[b] + kRectTileKeys - 1) / kRectTileKeys;
-      for (int g = 0; g < c.Hkv; ++g) {
-        const long long as = pt * Hkv + g * T;
-        long long wl, wh;
-        inner_bounds(as, as + T, P, TT, &wl, &wh);
-        cloc += 1 + (wh >= wl ? wh - wl + 1 : 0);
-      }
-      pt += T;
-    }
+  for (int s = s0; s < s1; ++s) {
+    long long as, es, wl, wh;
+    segment(s, as, es, wl, wh);
+    cloc += 1 + (wh >= wl ? wh - wl + 1 : 0);
   }
   long long nitems;
   long long fi = block_exclusive_scan(cloc, sh, &nitems);
-  {
-    long long pt = pt0;
-    for (int b = b0; b < b1; ++b) {
-      const int L = c.seq_lens[b];
-      const long long T = (L + kRectTileKeys - 1) / kRectTileKeys;
-      for (int g = 0; g < c.Hkv; ++g) {
-        const long long as = pt * Hkv + g * T, es = as + T;
-        long long wl, wh;
-        inner_bounds(as, es, P, TT, &wl, &wh);
-        const int cnt = 1 + int(wh >= wl ? wh - wl + 1 : 0);
-        a.groups[b * c.Hkv + g] = make_int2(int(fi), cnt);
-        for (int j = 0; j < cnt; ++j) {
-          const long long st = j == 0 ? as : (wl + j - 1) * TT / P;
-          const long long en = j == cnt - 1 ? es : (wl + j) * TT / P;
-          a.items[fi + j] = make_int4(b, g, int((st - as) * kRectTileKeys),
-                                      int(min((long long)L, (en - as) * kRectTileKeys)));
-          if (j > 0) a.wg_first[wl + j - 1] = int(fi + j);
-          else if ((wl - 1) * TT / P == as) a.wg_first[wl - 1] = int(fi);
-        }
-        fi += cnt;
+  for (int s = s0; s < s1; ++s) {
+    long long as, es, wl, wh;
+    segment(s, as, es, wl, wh);
+    const int b = s / c.Hkv, g = s % c.Hkv;
+    const int L = c.seq_lens[b];
+    const int cnt = 1 + int(wh >= wl ? wh - wl + 1 : 0);
+    a.groups[s] = make_int2(int(fi), cnt);
+    // the range that holds tile as starts exactly there: this item is its first
+    const long long wprev = wl - 1;
+    if (wprev * q + (wprev * r) / P == as) a.wg_first[wprev] = int(fi);
+    long long lo_next = wl * q + (wl * r) / P, rem = (wl * r) % P;  // lo(wl)
+    long long st = as;
+    for (int j = 0; j < cnt; ++j) {
+      const long long en = j == cnt - 1 ? es : lo_next;
+      a.items[fi + j] = make_int4(b, g, int((st - as) * kRectTileKeys),
+                                  int(min((long long)L, (en - as) * kRectTileKeys)));
+      if (j > 0) a.wg_first[wl + j - 1] = int(fi + j);
+      st = en;
+      lo_next += q;
+      rem += r;
+      if (rem >= P) {
+        lo_next += 1;
+        rem -= P;
       }
-      pt += T;
     }
+    fi += cnt;
   }
   for (long long w = P + tid; w <= a.slots; w += kPlanThreads) a.wg_first[w] = int(nitems);
 }
@@ -616,7 +636,7 @@ RectPlan plan_rectify(const CacheView& c, int f) {
 
 static size_t plan_bytes(const CacheView& c, const RectPlan& p) {
   return align_up(size_t(p.cap) * sizeof(int4), 256) + align_up(size_t(c.B) * c.Hkv * sizeof(int2), 256) +
-         align_up(size_t(p.slots + 1) * sizeof(int), 256);
+         align_up(size_t(p.slots + 1) * sizeof(int), 256) + align_up(size_t(c.B) * sizeof(long long), 256);
 }
 
 size_t rectify_ws_bytes(const CacheView& c, int f) {
@@ -644,6 +664,8 @@ hipError_t launch_rectify_attention(const CacheView& c, const void* q, int f, fl
   w += align_up(size_t(c.B) * c.Hkv * sizeof(int2), 256);
   a.wg_first = reinterpret_cast<int*>(w);
   w += align_up(size_t(p.slots + 1) * sizeof(int), 256);
+  a.ptile = reinterpret_cast<long long*>(w);
+  w += align_up(size_t(c.B) * sizeof(long long), 256);
   const size_t slots = size_t(p.cap) * p.rows_pad;
   a.part_ml = reinterpret_cast<float*>(w);
   a.part_acc = reinterpret_cast<float*>(w + align_up(slots * 2 * sizeof(float), 256));
