@@ -36,7 +36,7 @@ def _workloads():
     return {"gqa_128k": W.gqa_128k, "llama8b_32k": W.llama8b_32k, "long_256k": W.long_256k,
             "long_256k_r05": lambda: W.long_256k(r=0.05), "long_256k_f64": lambda: W.long_256k(f=64),
             "long_256k_r05_f64": lambda: W.long_256k(r=0.05, f=64),
-            "tiny_fp32": W.tiny_fp32, "rectify_mixed": W.rectify_mixed}
+            "tiny_fp32": W.tiny_fp32, "rectify_mixed": W.rectify_mixed, "prompt_32k": W.prompt_32k}
 
 
 # ---------------------------------------------------------------------------
@@ -204,6 +204,49 @@ def rectify_only(w, args):
         "cpu_baseline": None}))
 
 
+def prefill_only(w, args):
+    """Chunked prefill workload: the whole prompt is one unit (every chunk of f
+    positions through the rectification call, in order); repeated runs rewrite
+    the same rows, so each does identical work."""
+    import torch
+    from block_sparse_attention_quest_amd import workloads as W
+    from block_sparse_attention_quest_amd.schedule import ChunkedPrefill
+
+    K, Wu = args.steps, args.warmup
+    pf = ChunkedPrefill(w)
+    pf.stage(*W.prompt_inputs(w))
+    for _ in range(Wu):
+        pf.run()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(K):
+        pf.run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
+    B, T, d, Hq, Hkv = w.batch, pf.T, w.head_dim, w.num_q_heads, w.num_kv_heads
+    e = 2 if w.dtype == "bf16" else 4
+    flops = 4.0 * d * Hq * B * T * (T + 1) / 2
+    # each chunk reads the cache up to its end once
+    kv = sum(B * Hkv * (c0 + fc) * 2 * d * e for c0, fc in pf.chunks)
+    tflops = flops / (ms * 1e-3) / 1e12
+    gbs = kv / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "chunked prefill tokens/s (dense causal, one rectification call per chunk)",
+        "value": round(B * T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": Wu,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "prompt": T, "chunk": pf.chunk, "q_heads": Hq, "kv_heads": Hkv,
+                   "head_dim": d, "calls": len(pf.chunks)},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "flops_per_prefill": flops, "kv_bytes_per_prefill": kv},
+        "cpu_baseline": None}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -228,6 +271,8 @@ def main():
     torch.cuda.set_device(0)
     K, Wu = args.steps, args.warmup
     base = _workloads()[args.workload]()
+    if args.workload.startswith("prompt"):
+        return prefill_only(base, args)
     if base.steps == 0:
         return rectify_only(base, args)
     w = base.replace(steps=Wu + K + MEASURE_STEPS)

@@ -370,7 +370,9 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_rect_mfma(RectArgs a) {
     // softmax of tile t and its O^T update
     auto consume = [&](int t, f32x16_t& sacc, const uint4* vst) {
       const int base = key_lo + t * kRectTileKeys;
-      if (base + kRectTileKeys > first_masked || base + kRectTileKeys > key_hi) {  // wave-uniform
+      // wave-uniform: the tile reaches the causal diagonal or the end
+      const bool edge = base + kRectTileKeys > first_masked || base + kRectTileKeys > key_hi;
+      if (edge) {
         int k0 = 8 * half;
         asm volatile("" : "+v"(k0));
         // highest key this lane's row may see, relative to the lane's first key
@@ -404,6 +406,27 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_rect_mfma(RectArgs a) {
         }
         pb[k2] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
       }
+      // Rows near the diagonal may see only a few keys, where one probability's
+      // bf16 rounding is not averaged out; there p also goes in as the bf16
+      // pair hi + lo (hi = bf16(p), lo = bf16(p - hi)), about 16 bits of p.
+      bf16x8_t pl[2];
+      if (edge) {
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          uint32_t w[4];
+          const uint4 hw = __builtin_bit_cast(uint4, pb[k2]);
+          const uint32_t hv[4] = {hw.x, hw.y, hw.z, hw.w};
+#pragma unroll
+          for (int x2 = 0; x2 < 4; ++x2) {
+            const f32x2_t lr = {p[8 * k2 + 2 * x2] - __uint_as_float(hv[x2] << 16),
+                                p[8 * k2 + 2 * x2 + 1] - __uint_as_float(hv[x2] & 0xffff0000u)};
+            w[x2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lr, bf16x2_t));
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[x2]),
+                                                   __builtin_bit_cast(bf16x2_t, ones), lsum, false);
+          }
+          pl[k2] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+        }
+      }
       const uint4* vl = vst + (half * D + col);
 #pragma unroll
       for (int tt = 0; tt < DT; ++tt)
@@ -413,6 +436,15 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_rect_mfma(RectArgs a) {
           const uint4 vv = vl[2 * k2 * D + tt * 32];
           o[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vv), pb[k2], o[tt], 0, 0, 0);
         }
+      if (edge) {
+#pragma unroll
+        for (int tt = 0; tt < DT; ++tt)
+#pragma unroll
+          for (int k2 = 0; k2 < 2; ++k2) {
+            const uint4 vv = vl[2 * k2 * D + tt * 32];
+            o[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vv), pl[k2], o[tt], 0, 0, 0);
+          }
+      }
     };
 
     // Pipeline: NS - 1 tiles are requested ahead. At step t the wave waits for

@@ -135,3 +135,55 @@ class ResaRunner:
                 ro = self.rectify(t, *self.rectify_inputs(t))
                 if on_rectify is not None:
                     on_rectify(t, ro)
+
+
+class ChunkedPrefill:
+    """Dense causal prefill through the rectification call ("Rectified Sparse
+    Attention": rectification re-encodes recent tokens with the dense pass;
+    prefill is that pass over the whole prompt). An equal-length batch of
+    T-token prompts goes through resa_rectify in chunks of at most `chunk`
+    (<= 64) positions: each call writes its chunk's K/V into the pages,
+    refreshes the touched blocks' descriptors (so the whole cache's descriptors
+    are built when the last chunk lands) and returns the chunk's causal
+    attention rows. Prompts of different lengths are prefilled per length.
+    """
+
+    def __init__(self, w: W.Workload, chunk: Optional[int] = None, device="cuda"):
+        self.w = w
+        self.device = device
+        self.chunk = w.f if chunk is None else chunk
+        B, Hq, Hkv, d = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim
+        self.T = w.prefill_lens[0]
+        if any(L != self.T for L in w.prefill_lens):
+            raise ValueError("ChunkedPrefill takes prompts of one length")
+        self.cache = R.PagedKVCache(B, Hq, Hkv, d, w.num_pages, w.max_blocks_per_seq, w.max_seq_len,
+                                    dtype=w.torch_dtype, device=device)
+        self.cache.block_table.copy_(W.block_table(w))
+        self.chunks = [(c0, min(self.chunk, self.T - c0)) for c0 in range(0, self.T, self.chunk)]
+        # sequence lengths once chunk i is in: one device row per chunk
+        self.lens = torch.tensor([[c0 + fc] * B for c0, fc in self.chunks], dtype=torch.int32, device=device)
+        self.cache.c.seq_lens = self.lens[0].data_ptr()
+        self.ws = R.workspace(R.resa_rectify_workspace_size(self.cache, self.chunk), device)
+        self.scale = 1.0 / math.sqrt(d)
+        self.inputs = []
+        self.outs = []
+
+    def stage(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor) -> None:
+        """Chunk-major device copies of the prompt ([B][T][H][d] each): every
+        chunk's rows contiguous as the call expects."""
+        self.inputs = [tuple(x[:, c0:c0 + fc].contiguous().to(self.device) for x in (q, k, v))
+                       for c0, fc in self.chunks]
+        self.outs = [torch.empty(self.w.batch, fc, self.w.num_q_heads, self.w.head_dim, dtype=self.w.torch_dtype,
+                                 device=self.device) for _, fc in self.chunks]
+
+    def run(self, stream=None):
+        """Every chunk in order; returns the per-chunk outputs [B][fc][Hq][d]."""
+        for i, (c0, fc) in enumerate(self.chunks):
+            self.cache.c.seq_lens = self.lens[i].data_ptr()
+            qc, kc, vc = self.inputs[i]
+            R.resa_rectify(self.cache, qc, kc, vc, fc, self.outs[i], self.ws, self.scale, stream=stream)
+        return self.outs
+
+    def output(self) -> torch.Tensor:
+        """The prompt's attention outputs [B][T][Hq][d]."""
+        return torch.cat(self.outs, dim=1)

@@ -243,6 +243,31 @@ def rectify_only_inputs(w: Workload) -> Tuple[torch.Tensor, torch.Tensor, torch.
     return q.to(w.torch_dtype), k.to(w.torch_dtype), v.to(w.torch_dtype)
 
 
+def prompt_inputs(w: Workload) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Prompt of a prefill workload (every sequence prefill_lens[0] tokens):
+    queries [B][T][Hq][d] ~ N(0, 1) and the prompt K/V [B][T][Hkv][d], the same
+    draws as prefill_kv, so a chunked prefill leaves the cache that fill-in
+    would have written."""
+    T = w.prefill_lens[0]
+    if any(L != T for L in w.prefill_lens):
+        raise ValueError("a prefill workload holds equal-length prompts")
+    q = _randn((w.batch, T, w.num_q_heads, w.head_dim), w.seed, "prompt_q")
+    ks, vs = [], []
+    for b in range(w.batch):
+        kv = [prefill_kv(w, b, h) for h in range(w.num_kv_heads)]
+        ks.append(torch.stack([k for k, _ in kv], dim=1))
+        vs.append(torch.stack([v for _, v in kv], dim=1))
+    return q.to(w.torch_dtype), torch.stack(ks), torch.stack(vs)
+
+
+def prompt_32k(**kw) -> Workload:
+    """Chunked prefill of one 32768-token prompt, 32q/8kv, d 128, bf16, in
+    chunks of f = 64 positions."""
+    w = Workload("gqa32x8_d128_bf16_b1_prompt32k_chunk64", "bf16", 1, 32, 8, 128, (32768,), 0, 64, 16, 0.1, 1,
+                 (0,), True, 7)
+    return w.replace(**kw) if kw else w
+
+
 def block_table(w: Workload) -> torch.Tensor:
     """[B][max_blocks_per_seq] int32: a seeded permutation of the page pool."""
     perm = torch.randperm(w.num_pages, generator=_gen(w.seed, "block_table"))

@@ -51,7 +51,7 @@ def _check_group_step(w, r_bt, desc_g, idx, count, out, q, b, g, K, V):
     sel = idx[b, g, :n]
     ties = P.assert_selection_valid(sel, M, n, w.n_local, s, qbar, kmin, kmax)
     ref = O.sparse_decode_group(qg, K, V, sel.tolist(), 1.0 / math.sqrt(w.head_dim))
-    err = np.abs(P.f64(out[b, g * G:(g + 1) * G]) - ref).max()
+    err = P.out_error(P.f64(out[b, g * G:(g + 1) * G]), ref, w.dtype)
     assert err <= P.ATOL[w.dtype], err
     return err, ties
 
@@ -117,7 +117,7 @@ def test_decode_and_rectify_sampled(make):
         for i in (0, w.f // 2, w.f - 1):
             for h in range(g * w.group, (g + 1) * w.group):
                 ref = O.causal_rows(P.f64(rq[b, i:i + 1, h]), K, V, L - w.f + i, scale)[0]
-                err = np.abs(P.f64(got[b, i, h]) - ref).max()
+                err = P.out_error(P.f64(got[b, i, h]), ref, w.dtype)
                 assert err <= P.ATOL[w.dtype], (b, i, h, err)
         print(f"[result] rectify rows of group {(b, g)} ok", flush=True)
 
@@ -143,6 +143,6 @@ def test_rectify_mixed_sampled():
         for i in (0, 31, 63):
             for h in (g * w.group, (g + 1) * w.group - 1):
                 ref = O.causal_rows(P.f64(q[b, i:i + 1, h]), K, V, L - w.f + i, scale)[0]
-                err = np.abs(P.f64(got[b, i, h]) - ref).max()
+                err = P.out_error(P.f64(got[b, i, h]), ref, "bf16")
                 assert err <= P.ATOL["bf16"], (b, i, h, err)
         print(f"[result] group {(b, g)} (L={L}) ok", flush=True)
