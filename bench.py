@@ -247,12 +247,106 @@ def prefill_only(w, args):
         "cpu_baseline": None}))
 
 
+def sweep(args):
+    """Context-length sweep at batch 1 (32q/8kv, d 128, bf16), the kernel-level
+    breakdown the pages plot ("Rectified Sparse Attention", Figure 6): dense
+    decode (every block, the same decode kernel), sparse decoding (append +
+    select + sparse decode, no rectification: f = infinity) at several active
+    ratios r, one rectification event at several f, and ReSA per step (sparse
+    step + rectification / f). Prints a markdown table and one JSON line per
+    context length."""
+    import torch
+    from block_sparse_attention_quest_amd import resa as R
+    from block_sparse_attention_quest_amd import workloads as W
+    from block_sparse_attention_quest_amd.schedule import ResaRunner
+
+    torch.cuda.set_device(0)
+    K, Wu = args.steps, args.warmup
+    ratios, fs = (0.05, 0.1, 0.2), (16, 32, 64, 128)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return 1e3 * e0.elapsed_time(e1) / n
+
+    rows = []
+    for L in (32768, 65536, 131072, 262144):
+        steps = len(ratios) * (Wu + K) + 2
+        w = W.long_256k(prefill_lens=(L,), steps=steps, r=1.0, f=64,
+                        planted=(int(round(0.01 * (L // 16))),))
+        print(f"[sweep] context {L}: setting up", file=sys.stderr, flush=True)
+        r = ResaRunner(w)
+        r.fill_prefill()
+        r.build_descriptors()
+        # dense decode: every block selected (r = 1), decode call only, at length L + 1
+        r.decode_step(0)
+        dense = timed(lambda i: R.resa_sparse_decode(r.cache, r.step_inputs["q"][0], r.idx, r.count, r.n_cap,
+                                                     r.out, r.ws, r.scale), K)
+        t = 1
+        sparse = {}
+        for rv in ratios:
+            # the index buffer sized for this ratio: the decode call splits its
+            # work by the capacity n_cap it is given
+            r.params = R.make_params(w.n_min, rv, w.n_local)
+            r.n_cap = R.resa_n_cap(r.cache, r.params)
+            r.idx = torch.full((w.batch, w.num_kv_heads, r.n_cap), -1, dtype=torch.int32, device="cuda")
+            for _ in range(Wu):
+                r.decode_step(t)
+                t += 1
+            t0 = t
+            sparse[rv] = timed(lambda i: r.decode_step(t0 + i), K)
+            t += K
+        # one rectification of the f newest tokens (f = 128 as two calls of 64)
+        rect = {}
+        for f in fs:
+            g = torch.Generator().manual_seed(f)
+            n64 = (f + 63) // 64
+            ins = [tuple(torch.randn(1, min(64, f), hh, 128, generator=g).to(torch.bfloat16).cuda()
+                         for hh in (32, 8, 8)) for _ in range(n64)]
+
+            def event(_i, ins=ins, f=f, n64=n64):
+                for c in range(n64):
+                    fc = min(64, f - 64 * c)
+                    # the c-th call ends (n64 - 1 - c) * 64 tokens before the newest
+                    row = t - (n64 - 1 - c) * 64
+                    r.rectify(row - 1, *ins[c], f=fc)
+            event(0)
+            rect[f] = timed(event, max(4, K // 8))
+        row = {"context": L, "dense_decode_us": round(dense, 1),
+               **{f"sparse_r{rv}_us": round(sparse[rv], 1) for rv in ratios},
+               **{f"rectify_f{f}_us": round(rect[f], 1) for f in fs}}
+        for f in fs:
+            resa = sparse[0.1] + rect[f] / f
+            row[f"resa_r0.1_f{f}_us"] = round(resa, 1)
+            row[f"rectify_share_f{f}"] = round(rect[f] / f / resa, 3)
+        row["speedup_dense_over_resa_f32"] = round(dense / (sparse[0.1] + rect[32] / 32), 2)
+        rows.append(row)
+        print(json.dumps(row), flush=True)
+        del r
+        torch.cuda.empty_cache()
+    cols = ["context", "dense_decode_us"] + [f"sparse_r{rv}_us" for rv in ratios] + \
+           [f"rectify_f{f}_us" for f in fs] + [f"resa_r0.1_f{f}_us" for f in (32, 64)] + \
+           ["rectify_share_f32", "speedup_dense_over_resa_f32"]
+    print("| " + " | ".join(cols) + " |")
+    print("|" + "---|" * len(cols))
+    for row in rows:
+        print("| " + " | ".join(str(row[c]) for c in cols) + " |")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--workload", default="gqa_128k")
+    ap.add_argument("--sweep", action="store_true",
+                    help="context-length sweep at batch 1: dense / sparse / rectify breakdown (not the bench line)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -269,6 +363,8 @@ def main():
     from block_sparse_attention_quest_amd.schedule import ResaRunner
 
     torch.cuda.set_device(0)
+    if args.sweep:
+        return sweep(args)
     K, Wu = args.steps, args.warmup
     base = _workloads()[args.workload]()
     if args.workload.startswith("prompt"):
