@@ -146,6 +146,35 @@ __global__ __launch_bounds__(kScoreThreads) void k_score(CacheView c, const void
   }
 }
 
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t x) {
+  const int lo = __builtin_amdgcn_mov_dpp(int(uint32_t(x)), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_mov_dpp(int(uint32_t(x >> 32)), CTRL, 0xF, 0xF, false);
+  return (uint64_t(uint32_t(hi)) << 32) | uint32_t(lo);
+}
+
+// Maximum (MAX) or minimum over each row of 16 lanes, every lane of the row
+// gets it (four DPP steps).
+template <bool MAX>
+__device__ __forceinline__ uint64_t row_reduce_u64(uint64_t x) {
+  auto pick = [](uint64_t a, uint64_t b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
+  x = pick(x, dpp_u64<kDppQuadXor1>(x));
+  x = pick(x, dpp_u64<kDppQuadXor2>(x));
+  x = pick(x, dpp_u64<kDppHalfMirror>(x));
+  return pick(x, dpp_u64<kDppRowMirror>(x));
+}
+
+// The same over the 64 lanes of a wave: the rows, then two lane swaps across
+// rows.
+template <bool MAX>
+__device__ __forceinline__ uint64_t wave_reduce_u64(uint64_t x) {
+  auto pick = [](uint64_t a, uint64_t b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
+  x = row_reduce_u64<MAX>(x);
+  x = pick(x, uint64_t(__shfl_xor((unsigned long long)x, 16, 64)));
+  x = pick(x, uint64_t(__shfl_xor((unsigned long long)x, 32, 64)));
+  return x;
+}
+
 __device__ __forceinline__ uint64_t order_key(double s) {
   if (s == 0.0) s = 0.0;  // -0 and +0 are equal scores
   const uint64_t u = uint64_t(__double_as_longlong(s));
@@ -224,10 +253,7 @@ __global__ __launch_bounds__(kTopnThreads) void k_topn(const double* __restrict_
     for (int e = 0; e < EMAX; ++e) key[e] = order_key(sc[e]);
   }
   for (int i = tid; i < kTopnBins; i += kTopnThreads) sm.hist[i] = 0;
-  for (int i = tid; i < kBitmapWords; i += kTopnThreads) {
-    sm.sel[i] = 0;
-    sm.tie[i] = 0;
-  }
+  if (tid == 0) sm.gcount = 0;
 
   // mode: 0 none of the candidates, 1 every member of the prefix group,
   // 2 the lowest indices of the (exactly tied) prefix group, 3 ranked group
@@ -243,22 +269,19 @@ __global__ __launch_bounds__(kTopnThreads) void k_topn(const double* __restrict_
         kmin = key[e] < kmin ? key[e] : kmin;
       }
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const uint64_t x = __shfl_xor(kmax, o, 64), y = __shfl_xor(kmin, o, 64);
-      kmax = x > kmax ? x : kmax;
-      kmin = y < kmin ? y : kmin;
-    }
+    kmax = wave_reduce_u64<true>(kmax);
+    kmin = wave_reduce_u64<false>(kmin);
     if (lane == 0) {
       sm.red_max[wave] = kmax;
       sm.red_min[wave] = kmin;
     }
     __syncthreads();
-#pragma unroll
-    for (int w = 0; w < kTopnWaves; ++w) {
-      kmax = sm.red_max[w] > kmax ? sm.red_max[w] : kmax;
-      kmin = sm.red_min[w] < kmin ? sm.red_min[w] : kmin;
-    }
+    // lanes 0 .. 15 of every wave take one wave's result each, then reduce them
+    // inside the row of 16
+    kmax = sm.red_max[lane & (kTopnWaves - 1)];
+    kmin = sm.red_min[lane & (kTopnWaves - 1)];
+    kmax = row_reduce_u64<true>(kmax);
+    kmin = row_reduce_u64<false>(kmin);
     const int plen = kmax == kmin ? 64 : __clzll((long long)(kmax ^ kmin));
     mask = plen == 0 ? 0ull : (~0ull << (64 - plen));
     prefix = kmax & mask;
@@ -269,6 +292,7 @@ __global__ __launch_bounds__(kTopnThreads) void k_topn(const double* __restrict_
       const int nb = bits_left < kTopnBits ? bits_left : kTopnBits;
       const int shift = bits_left - nb;
       const int nbins = 1 << nb;
+      const bool first_pass = first;
       if (!first) {
         for (int i = tid; i < kTopnBins; i += kTopnThreads) sm.hist[i] = 0;
         __syncthreads();
@@ -276,7 +300,8 @@ __global__ __launch_bounds__(kTopnThreads) void k_topn(const double* __restrict_
       first = false;
 #pragma unroll
       for (int e = 0; e < EMAX; ++e) {
-        if (e * kTopnThreads + tid < Mo && (key[e] & mask) == prefix)
+        // the first pass takes every candidate: all share the range's prefix
+        if (e * kTopnThreads + tid < Mo && (first_pass || (key[e] & mask) == prefix))
           atomicAdd(&sm.hist[int(key[e] >> shift) & (nbins - 1)], 1);
       }
       __syncthreads();
@@ -307,53 +332,56 @@ __global__ __launch_bounds__(kTopnThreads) void k_topn(const double* __restrict_
       bits_left -= nb;
     }
     mode = gsize == k ? 1 : (bits_left == 0 ? 2 : 3);
-    if (mode == 3) {
-      if (tid == 0) sm.gcount = 0;
-      __syncthreads();
+  }
+  // mark the chosen blocks: a wave's 64 consecutive blocks are two bitmap
+  // words, stored whole by its first lane from ballots (each word has exactly
+  // one writer, so no clearing or atomics are needed); in mode 3 the members
+  // of the threshold's prefix group are gathered for ranking on the way
 #pragma unroll
-      for (int e = 0; e < EMAX; ++e) {
-        const int j = e * kTopnThreads + tid;
-        if (j < Mo && (key[e] & mask) == prefix) {
-          const int s = atomicAdd(&sm.gcount, 1);
-          sm.gk[s] = key[e];
-          sm.gj[s] = j;
-        }
+  for (int e = 0; e < EMAX; ++e) {
+    const int j = e * kTopnThreads + tid;
+    bool s = false, t = false;
+    if (j < Mo) {
+      const uint64_t km = key[e] & mask;
+      const bool above = km > prefix, at = km == prefix;
+      s = mode != 0 && (above || (at && mode == 1));
+      t = at && mode == 2;
+      if (at && mode == 3) {
+        const int slot = atomicAdd(&sm.gcount, 1);
+        sm.gk[slot] = key[e];
+        sm.gj[slot] = j;
       }
-      __syncthreads();
-      if (tid < 64) {
-        const int gs = sm.gcount;
-        if (tid < gs) {
-          const uint64_t kt = sm.gk[tid];
-          const int jt = sm.gj[tid];
-          int rank = 0;
-          for (int u = 0; u < gs; ++u) {
-            const uint64_t ku = sm.gk[u];
-            rank += (ku > kt || (ku == kt && sm.gj[u] < jt)) ? 1 : 0;
-          }
-          if (rank < k) atomicOr(&sm.sel[jt >> 5], 1u << (jt & 31));
-        }
+    } else if (j < M) {
+      s = true;
+    }
+    const uint64_t bs = __builtin_amdgcn_ballot_w64(s);
+    const int w0 = (e * kTopnThreads + wave * 64) >> 5;
+    if (lane == 0) {
+      sm.sel[w0] = uint32_t(bs);
+      sm.sel[w0 + 1] = uint32_t(bs >> 32);
+    }
+    if (mode == 2) {  // the tie words are read in mode 2 only
+      const uint64_t bt = __builtin_amdgcn_ballot_w64(t);
+      if (lane == 0) {
+        sm.tie[w0] = uint32_t(bt);
+        sm.tie[w0 + 1] = uint32_t(bt >> 32);
       }
     }
   }
   __syncthreads();
-  // mark the chosen blocks
-#pragma unroll
-  for (int e = 0; e < EMAX; ++e) {
-    const int j = e * kTopnThreads + tid;
-    if (j >= M) continue;
-    bool s = false, t = false;
-    if (j >= Mo) {
-      s = true;
-    } else if (mode != 0) {
-      const uint64_t km = key[e] & mask;
-      if (km > prefix) s = true;
-      else if (km == prefix) {
-        if (mode == 1) s = true;
-        else if (mode == 2) t = true;
-      }
+  if (mode == 3 && tid < 64) {  // wave 0 ranks the gathered group, one candidate per lane
+    const int gs = sm.gcount;
+    const uint64_t kt = tid < gs ? sm.gk[tid] : 0;
+    const int jt = tid < gs ? sm.gj[tid] : 0;
+    const uint32_t klo = uint32_t(kt), khi = uint32_t(kt >> 32);
+    int rank = 0;
+    for (int u = 0; u < gs; ++u) {  // candidate u broadcast from its lane
+      const uint64_t ku = (uint64_t(uint32_t(__builtin_amdgcn_readlane(khi, u))) << 32) |
+                          uint32_t(__builtin_amdgcn_readlane(klo, u));
+      const int ju = __builtin_amdgcn_readlane(jt, u);
+      rank += (ku > kt || (ku == kt && ju < jt)) ? 1 : 0;
     }
-    if (s) atomicOr(&sm.sel[j >> 5], 1u << (j & 31));
-    if (t) atomicOr(&sm.tie[j >> 5], 1u << (j & 31));
+    if (tid < gs && rank < k) atomicOr(&sm.sel[jt >> 5], 1u << (jt & 31));
   }
   __syncthreads();
   // exactly tied threshold group: the k lowest indices
@@ -373,7 +401,7 @@ __global__ __launch_bounds__(kTopnThreads) void k_topn(const double* __restrict_
   int total;
   int pos = wg_exclusive_scan(__builtin_popcount(word), sm.scan, total);
   int32_t* out = idx + gi * n_cap;
-  while (word) {
+  while (word && pos < n) {  // exactly n bits are set; the bound keeps every store in the row
     const int e = __builtin_ctz(word);
     word &= word - 1u;
     out[pos++] = tid * 32 + e;
@@ -387,14 +415,24 @@ hipError_t launch_topn(const CacheView& c, const resa_select_params& p, int32_t*
   dim3 grid(c.Hkv, c.B);
 #define RESA_TOPN(E) hipLaunchKernelGGL(k_topn<E>, grid, dim3(kTopnThreads), 0, s, scores, c.seq_lens, c.maxb, \
                                         c.Hkv, p, idx, count, n_cap)
-  if (e <= 2) RESA_TOPN(2);
-  else if (e <= 4) RESA_TOPN(4);
-  else if (e <= 8) RESA_TOPN(8);
-  else if (e <= 12) RESA_TOPN(12);
-  else if (e <= 16) RESA_TOPN(16);
-  else if (e <= 20) RESA_TOPN(20);
-  else if (e <= 24) RESA_TOPN(24);
-  else RESA_TOPN(32);
+  // every thread handles EMAX keys: exact up to 18 (256K context), then
+  // coarser steps
+  switch (e) {
+    case 0: case 1: case 2: RESA_TOPN(2); break;
+    case 3: case 4: RESA_TOPN(4); break;
+    case 5: case 6: RESA_TOPN(6); break;
+    case 7: case 8: RESA_TOPN(8); break;
+    case 9: RESA_TOPN(9); break;
+    case 10: RESA_TOPN(10); break;
+    case 11: case 12: RESA_TOPN(12); break;
+    case 13: case 14: RESA_TOPN(14); break;
+    case 15: case 16: RESA_TOPN(16); break;
+    case 17: RESA_TOPN(17); break;
+    case 18: RESA_TOPN(18); break;
+    case 19: case 20: RESA_TOPN(20); break;
+    case 21: case 22: case 23: case 24: RESA_TOPN(24); break;
+    default: RESA_TOPN(32); break;
+  }
 #undef RESA_TOPN
   return hipGetLastError();
 }
