@@ -32,7 +32,7 @@ namespace resa {
 namespace {
 
 constexpr int kPlanThreads = 1024;
-constexpr int kMaxItemTiles = 512;  // tiles per workgroup range (16384 keys)
+constexpr int kMaxItemTiles = 1024;  // tiles per workgroup range (32768 keys)
 
 struct RectArgs {
   CacheView c;
@@ -78,8 +78,9 @@ __device__ long long block_exclusive_scan(long long v, long long* sh, long long*
 // Work plan of one rectification, built on the device from seq_lens.
 // Segment s = (sequence b, KV head g) covers T_b = ceil(L_b / 32) key tiles;
 // segments in order (b, then g) make one line of TT tiles, split into P equal
-// workgroup ranges at lo(w) = floor(w TT / P). P is the target, raised so that
-// no range exceeds kMaxItemTiles, and at most TT. Items are the pieces of the
+// workgroup ranges at lo(w) = floor(w TT / P). P is the fewest whole rounds
+// of the target count that keep every range within kMaxItemTiles (so all
+// workgroups of a round finish together), and at most TT. Items are the pieces of the
 // line cut at segment starts and range starts, in line order; the item that
 // starts a range is that workgroup's first. Boundaries inside segment [a, e)
 // are lo(w) for w in [ceil((a+1) P / TT), ceil(e P / TT) - 1]. Threads take
@@ -103,8 +104,8 @@ __global__ __launch_bounds__(kPlanThreads) void k_rect_plan(RectArgs a) {
     pt += tiles(b);
   }
   const long long TT = tsum * Hkv;
-  long long P = ceil_div_ll(TT, kMaxItemTiles);
-  if (P < a.target) P = a.target;
+  // whole rounds of `target` workgroups, as few as keep ranges <= kMaxItemTiles
+  long long P = a.target * ceil_div_ll(TT, (long long)a.target * kMaxItemTiles);
   if (P > TT) P = TT;
   const long long q = TT / P, r = TT % P;
   __syncthreads();  // ptile visible to the workgroup
@@ -656,12 +657,12 @@ RectPlan plan_rectify(const CacheView& c, int f) {
   p.rows_pad = (p.rows + 31) / 32 * 32;
   // one round of workgroups: two per CU with 4 waves (<= 128 rows), one with 8
   p.target = p.rows_pad <= 128 ? 512 : 256;
-  // the plan raises the count so that no range exceeds kMaxItemTiles tiles;
-  // the launch covers the largest cache the capacities allow
+  // the plan adds whole rounds of workgroups while a range would exceed
+  // kMaxItemTiles tiles; the launch covers the largest cache the capacities allow
   const long long groups = (long long)c.B * c.Hkv;
   const long long tt_max = groups * ((c.max_seq_len + kRectTileKeys - 1) / kRectTileKeys);
-  const long long need = (tt_max + kMaxItemTiles - 1) / kMaxItemTiles;
-  p.slots = int(need > p.target ? need : p.target);
+  const long long rounds = (tt_max + (long long)p.target * kMaxItemTiles - 1) / ((long long)p.target * kMaxItemTiles);
+  p.slots = int(p.target * (rounds > 0 ? rounds : 1));
   p.cap = p.slots + int(groups);  // items: one per range plus one per (sequence, KV head)
   return p;
 }
