@@ -120,6 +120,28 @@ class PagedKVCache:
         return self.c
 
 
+class CacheSubset:
+    """The cache descriptor of the contiguous sequences [b0, b1) of a
+    PagedKVCache: the same pages, that range's block-table rows and lengths
+    (pointer offsets into the parent's arrays, taken from the parent's current
+    descriptor at every use). Any call can run on it, e.g. a rectification of
+    the sequences that are due while the others keep decoding."""
+
+    def __init__(self, cache: PagedKVCache, b0: int, b1: int):
+        if not 0 <= b0 < b1 <= cache.batch:
+            raise ValueError(f"sequence range [{b0}, {b1}) outside the batch of {cache.batch}")
+        self.parent, self.b0, self.b1 = cache, b0, b1
+        self.batch = b1 - b0
+        self.head_dim = cache.head_dim
+
+    @property
+    def struct(self) -> ResaCache:
+        c = self.parent.c
+        return ResaCache(c.dtype, self.batch, c.num_q_heads, c.num_kv_heads, c.head_dim, c.block_size, c.num_pages,
+                         c.max_blocks_per_seq, c.max_seq_len, c.k_pages, c.v_pages, c.desc,
+                         c.block_table + self.b0 * c.max_blocks_per_seq * 4, c.seq_lens + self.b0 * 4)
+
+
 def make_params(n_min: int, r: float, n_local: int) -> ResaSelectParams:
     return ResaSelectParams(int(n_min), int(n_local), float(r))
 

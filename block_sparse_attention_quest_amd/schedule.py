@@ -112,6 +112,17 @@ class ResaRunner:
         R.resa_rectify(self.cache, q, k, v, f, out, self.ws, self.scale)
         return out
 
+    def rectify_subset(self, t: int, b0: int, b1: int, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                       f: Optional[int] = None) -> torch.Tensor:
+        """Rectify only sequences [b0, b1) after decode step t (the others
+        keep their sparse-phase rows); q [b1-b0][f][Hq][d], k, v [b1-b0][f][Hkv][d]."""
+        f = self.w.f if f is None else f
+        self.set_step_lens(t + 1)
+        out = torch.empty(b1 - b0, f, self.w.num_q_heads, self.w.head_dim, dtype=self.w.torch_dtype,
+                          device=self.device)
+        R.resa_rectify(R.CacheSubset(self.cache, b0, b1), q, k, v, f, out, self.ws, self.scale)
+        return out
+
     def rectify_only(self) -> torch.Tensor:
         """Rectify-only workload: the f newest tokens of every sequence (beyond the
         prefill) are written, their blocks refreshed, and their rows attended."""

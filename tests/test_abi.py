@@ -127,3 +127,17 @@ def test_update_descriptor_argument_checks(lib):
     assert lib.resa_update_descriptors(ctypes.byref(c), buf, None, 1, None) == R.RESA_ERR_INVALID
     assert lib.resa_update_descriptors(ctypes.byref(c), buf, buf, 0, None) == R.RESA_ERR_INVALID
     assert lib.resa_update_descriptors(ctypes.byref(c), None, None, -1, None) == R.RESA_ERR_INVALID
+
+
+def test_cache_subset_offsets_pointers():
+    """A sub-batch view keeps the pages and offsets the block-table and length
+    pointers to its first sequence (no device memory is touched)."""
+    class _Parent:
+        batch, head_dim = 4, 128
+        c = _cache(batch=4)
+    sub = R.CacheSubset(_Parent, 1, 3)
+    s = sub.struct
+    assert (s.batch, s.k_pages, s.v_pages, s.desc) == (2, 0x1000, 0x2000, 0x3000)
+    assert s.block_table == 0x4000 + 1 * 32 * 4 and s.seq_lens == 0x5000 + 4
+    with pytest.raises(ValueError):
+        R.CacheSubset(_Parent, 3, 5)

@@ -154,6 +154,32 @@ def test_rectify_mixed_lengths_small():
     P.assert_desc_equal(r.cache.desc, oc)
 
 
+def test_rectify_of_some_sequences_then_decode():
+    """Continuous batching: sequences 1 .. 2 of 3 are rectified through a
+    sub-batch view of the cache while sequence 0 is not; decoding of all three
+    then continues on the updated cache."""
+    w = W.Workload("sub_batch", "bf16", 3, 8, 2, 128, (200, 517, 64), 6, 4, 4, 0.2, 1, (0, 1, 0), True, 12)
+    r = _runner(w)
+    oc = P.oracle_cache(w)
+    atol = P.ATOL[w.dtype]
+    for t in range(6):
+        q, k, v = W.query(w, t), *W.append_kv(w, t)
+        O.append(oc, P.f64(k), P.f64(v))
+        out = r.decode_step(t)
+        torch.cuda.synchronize()
+        P.check_select_and_decode(oc, P.f64(q), w, r.idx, r.count, out, atol)
+        if t == 3:
+            rq, rk, rv = (x[1:3, :w.f].contiguous() for x in _rect_inputs(w, w.f, seed=5))
+            got = r.rectify_subset(t, 1, 3, rq.cuda(), rk.cuda(), rv.cuda())
+            sub = O.PagedCache(oc.k, oc.v, oc.desc, oc.block_table[1:3], oc.seq_lens[1:3])
+            ref = O.rectify(sub, P.f64(rq), P.f64(rk), P.f64(rv), 1.0 / math.sqrt(w.head_dim))
+            oc.k, oc.v, oc.desc = sub.k, sub.v, sub.desc
+            torch.cuda.synchronize()
+            err = P.out_error(P.f64(got), ref, "bf16")
+            assert err <= atol, err
+            P.assert_desc_equal(r.cache.desc, oc)
+
+
 def test_decode_is_deterministic():
     w = W.Workload("det", "bf16", 2, 8, 2, 128, (3000, 1234), 3, 0, 16, 0.1, 1, (5, 5), True, 9)
     outs = []
