@@ -330,7 +330,7 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_rect_mfma(RectArgs a) {
     // The lane offsets pass through an empty asm at every use, so the compiler
     // adds them to each stage's base where they are read instead of keeping a
     // precomputed address per stage and k-step live across the loop.
-    auto score = [&](f32x16_t& acc, const uint4* kst) {
+    auto score_operands = [&](bf16x8_t (&ak)[KSTEPS], const uint4* kst) {
       uint32_t ko[KSTEPS];
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
@@ -338,18 +338,19 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_rect_mfma(RectArgs a) {
         asm volatile("" : "+v"(ko[ks]));
       }
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        const bf16x8_t ak =
-            __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(kst) + ko[ks]));
-        if (ks == 0) {
-          f32x16_t z;
+      for (int ks = 0; ks < KSTEPS; ++ks)
+        ak[ks] = __builtin_bit_cast(bf16x8_t,
+                                    *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(kst) + ko[ks]));
+    };
+    auto score = [&](f32x16_t& acc, const uint4* kst) {
+      bf16x8_t ak[KSTEPS];
+      score_operands(ak, kst);
+      f32x16_t z;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) z[r] = 0.f;
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[0], z, 0, 0, 0);
-        } else {
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[ks], acc, 0, 0, 0);
-        }
-      }
+      for (int r = 0; r < 16; ++r) z[r] = 0.f;
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[0], qreg[0], z, 0, 0, 0);
+#pragma unroll
+      for (int ks = 1; ks < KSTEPS; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[ks], qreg[ks], acc, 0, 0, 0);
     };
 
     auto rescale = [&](float tmax) {
@@ -367,9 +368,15 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_rect_mfma(RectArgs a) {
       return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     };
 
-    // softmax of tile t and its O^T update
-    // softmax of tile t and its O^T update
-    auto consume = [&](int t, f32x16_t& sacc, const uint4* vst) {
+    // One pipeline step's work: the softmax of tile t (scores in sacc), the
+    // score products of tile t + 1 (into snext, from K stage kst; past the end
+    // a requested but unused tile), and the O^T update of tile t (V stage vst).
+    // The exponentials and packing of tile t are interleaved one MFMA at a time
+    // with the next tile's products, so the matrix cores and the VALU work
+    // together within the wave.
+    auto step_compute = [&](int t, f32x16_t& sacc, f32x16_t& snext, const uint4* kst, const uint4* vst) {
+      bf16x8_t ak[KSTEPS];
+      score_operands(ak, kst);
       const int base = key_lo + t * kRectTileKeys;
       // wave-uniform: the tile reaches the causal diagonal or the end
       const bool edge = base + kRectTileKeys > first_masked || base + kRectTileKeys > key_hi;
@@ -390,6 +397,13 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_rect_mfma(RectArgs a) {
       if (__builtin_amdgcn_ballot_w64(tmax > m + kLazy)) rescale(tmax);
       // a row that has seen no key yet (m = -inf) has only masked logits here
       const float nm = m == -__builtin_inff() ? 0.f : -m;
+      f32x16_t z;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) z[r] = 0.f;
+      snext = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[0], qreg[0], z, 0, 0, 0);
+#pragma unroll
+      for (int ks = 1; ks < KSTEPS; ++ks)
+        snext = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[ks], qreg[ks], snext, 0, 0, 0);
       float p[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(sacc[r], a.scale_log2, nm));
@@ -406,6 +420,12 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_rect_mfma(RectArgs a) {
                                                  __builtin_bit_cast(bf16x2_t, ones), lsum, false);
         }
         pb[k2] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+      }
+      // interleave: each score product with a share of the softmax arithmetic
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 48 / KSTEPS, 0);    // then VALU
       }
       // Rows near the diagonal may see only a few keys, where one probability's
       // bf16 rounding is not averaged out; there p also goes in as the bf16
@@ -494,14 +514,13 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_rect_mfma(RectArgs a) {
         }
         issue_tile(t + NS - 1, pick<SR>(st0, st1, st2, st3, st4, st5, st6, st7),
                    pick<SR>(st0, st1, st2, st3, st4, st5, st6, st7) + PIECES);
-        if (has_rows) {
-          if constexpr (S.value % 2 == 0) {
-            if (t + 1 < ntiles) score(s1, pick<SN>(st0, st1, st2, st3, st4, st5, st6, st7));
-            if (t < ntiles) consume(t, s0, pick<S.value>(st0, st1, st2, st3, st4, st5, st6, st7) + PIECES);
-          } else {
-            if (t + 1 < ntiles) score(s0, pick<SN>(st0, st1, st2, st3, st4, st5, st6, st7));
-            if (t < ntiles) consume(t, s1, pick<S.value>(st0, st1, st2, st3, st4, st5, st6, st7) + PIECES);
-          }
+        if (has_rows && t < ntiles) {
+          if constexpr (S.value % 2 == 0)
+            step_compute(t, s0, s1, pick<SN>(st0, st1, st2, st3, st4, st5, st6, st7),
+                         pick<S.value>(st0, st1, st2, st3, st4, st5, st6, st7) + PIECES);
+          else
+            step_compute(t, s1, s0, pick<SN>(st0, st1, st2, st3, st4, st5, st6, st7),
+                         pick<S.value>(st0, st1, st2, st3, st4, st5, st6, st7) + PIECES);
         }
       });
     }
