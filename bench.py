@@ -29,6 +29,8 @@ METRIC = "GBSA decode steps/s + achieved HBM GB/s at 128K ctx (32q/8kv, d=128)"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 MEASURE_STEPS = 64
+COLD_REPS = 16
+QUEUE_AHEAD_CYCLES = 100_000_000  # about 40 ms of spinning: covers queueing the measured steps
 
 
 def _workloads():
@@ -347,6 +349,8 @@ def main():
     ap.add_argument("--workload", default="gqa_128k")
     ap.add_argument("--sweep", action="store_true",
                     help="context-length sweep at batch 1: dense / sparse / rectify breakdown (not the bench line)")
+    ap.add_argument("--unfused-append", action="store_true",
+                    help="append with resa_update_descriptors, then resa_select_blocks (two calls)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -375,7 +379,7 @@ def main():
     t_setup = time.perf_counter()
     print(f"[bench] setting up {w.name}: batch {w.batch}, prefill {w.prefill_lens[0]}, steps {w.steps}",
           file=sys.stderr, flush=True)
-    r = ResaRunner(w)
+    r = ResaRunner(w, fused_append=not args.unfused_append)
     r.fill_prefill()
     r.build_descriptors()
     rect_steps = [t for t in range(w.steps) if w.f > 0 and (t + 1) % w.f == 0]
@@ -396,12 +400,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst, junk
 
-    def step(t, ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+    def step(t):
         r.decode_step(t)
-        if ev is not None:
-            ev[1].record(stream)
         if t in rect_in:
             r.rectify(t, *rect_in[t])
 
@@ -410,26 +410,33 @@ def main():
     torch.cuda.synchronize()
 
     def step_calls(t, ev=None):
-        """One whole step through the C ABI; with `ev`, events bracket every call."""
+        """One whole step through the C ABI. With `ev` (8 events): a pair around
+        each call, and an empty pair between the calls that measures what a
+        pair of event records costs on its own in the same queue."""
         r.set_step_lens(t + 1)
         q = r.step_inputs["q"][t]
+        k, v = r.step_inputs["k"][t], r.step_inputs["v"][t]
         if ev is not None:
             ev[0].record(stream)
-        R.resa_update_descriptors(r.cache, r.step_inputs["k"][t], r.step_inputs["v"][t], 1)
+        if r.fused_append:
+            R.resa_append_select(r.cache, k, v, q, r.params, r.idx, r.count, r.n_cap, r.ws)
+        else:
+            R.resa_update_descriptors(r.cache, k, v, 1)
+            R.resa_select_blocks(r.cache, q, r.params, r.idx, r.count, r.n_cap, r.ws)
         if ev is not None:
             ev[1].record(stream)
-        R.resa_select_blocks(r.cache, q, r.params, r.idx, r.count, r.n_cap, r.ws)
-        if ev is not None:
             ev[2].record(stream)
+            ev[3].record(stream)
+            ev[4].record(stream)
         R.resa_sparse_decode(r.cache, q, r.idx, r.count, r.n_cap, r.out, r.ws, r.scale)
         if ev is not None:
-            ev[3].record(stream)
+            ev[5].record(stream)
         if t in rect_in:
             if ev is not None:
-                ev[4].record(stream)
+                ev[6].record(stream)
             r.rectify(t, *rect_in[t])
             if ev is not None:
-                ev[5].record(stream)
+                ev[7].record(stream)
 
     # ---- timed region: K whole steps; events only at its two ends ----
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -444,23 +451,66 @@ def main():
 
     # ---- per-call durations: MEASURE_STEPS more steps, HIP events around every
     # call on the launch stream, queued without per-step synchronisation ----
+    # A spin kernel holds the GPU while the host queues every measured step, so
+    # that no call waits on its own submission (at small batch the host's
+    # per-step cost exceeds the GPU's); `ahead` records whether it held long
+    # enough.
+    torch.cuda._sleep(QUEUE_AHEAD_CYCLES)
+    held = torch.cuda.Event()
+    held.record(stream)
     evs = []
     for i in range(MEASURE_STEPS):
         t = Wu + K + i
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
         step_calls(t, ev)
         evs.append((t, ev))
+    ahead = not held.query()
     torch.cuda.synchronize()
-    times = {"append": [], "select": [], "decode": [], "rectify": []}
+    times = {"append_select": [], "decode": [], "rectify": []}
+    pairs = []
     for t, ev in evs:
-        times["append"].append(ev[0].elapsed_time(ev[1]))
-        times["select"].append(ev[1].elapsed_time(ev[2]))
-        times["decode"].append(ev[2].elapsed_time(ev[3]))
+        times["append_select"].append(ev[0].elapsed_time(ev[1]))
+        pairs.append(ev[2].elapsed_time(ev[3]))
+        times["decode"].append(ev[4].elapsed_time(ev[5]))
         if t in rect_in:
-            times["rectify"].append(ev[4].elapsed_time(ev[5]))
-    stage_us = {k: (1e3 * sum(v) / len(v) if v else None) for k, v in times.items()}
+            times["rectify"].append(ev[6].elapsed_time(ev[7]))
+    pair_us = 1e3 * sum(pairs) / len(pairs)
+    # a call's launch duration: its event-pair time less an empty pair's
+    stage_us = {k: (1e3 * sum(v) / len(v) - pair_us if v else None) for k, v in times.items()}
     dec_ms = stage_us["decode"] * 1e-3
-    sel_ms = stage_us["select"] * 1e-3
+    sel_ms = stage_us["append_select"] * 1e-3
+
+    # ---- cold-cache durations: the last step's calls again (both idempotent),
+    # each after a 1 GiB read that evicts L2 and the 256 MB last-level cache
+    # with clean lines (a write would leave dirty lines whose write-back then
+    # competes with the timed call), so none of the step's working set is
+    # cached when the call starts ----
+    flush = torch.ones((1 << 30) // 4, dtype=torch.float32, device="cuda")
+    sink = torch.empty(1, dtype=torch.float32, device="cuda")
+    t_last = Wu + K + MEASURE_STEPS - 1
+    cold_ev = []
+    q_last = r.step_inputs["q"][t_last]
+    k_last, v_last = r.step_inputs["k"][t_last], r.step_inputs["v"][t_last]
+    r.set_step_lens(t_last + 1)
+    for i in range(COLD_REPS):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        torch.sum(flush, dim=0, keepdim=True, out=sink)
+        ev[0].record(stream)
+        if r.fused_append:
+            R.resa_append_select(r.cache, k_last, v_last, q_last, r.params, r.idx, r.count, r.n_cap, r.ws)
+        else:
+            R.resa_update_descriptors(r.cache, k_last, v_last, 1)
+            R.resa_select_blocks(r.cache, q_last, r.params, r.idx, r.count, r.n_cap, r.ws)
+        ev[1].record(stream)
+        torch.sum(flush, dim=0, keepdim=True, out=sink)
+        ev[2].record(stream)
+        R.resa_sparse_decode(r.cache, q_last, r.idx, r.count, r.n_cap, r.out, r.ws, r.scale)
+        ev[3].record(stream)
+        cold_ev.append(ev)
+    torch.cuda.synchronize()
+    cold_us = {"append_select": 1e3 * sum(e[0].elapsed_time(e[1]) for e in cold_ev) / COLD_REPS - pair_us,
+               "decode": 1e3 * sum(e[2].elapsed_time(e[3]) for e in cold_ev) / COLD_REPS - pair_us}
+    del flush, sink
 
     # ---- algorithmic work at the middle of the timed region ----
     tm = Wu + K // 2
@@ -471,7 +521,7 @@ def main():
     full_cache = sum(w.num_kv_heads * L * 2 * w.head_dim * (2 if w.dtype == "bf16" else 4) for L in L_list)
     step_alg = sb["append"] + sb["select"] + sb["decode"] + (rkv / w.f if w.f > 0 else 0)
     dec_gbs = sb["decode"] / (dec_ms * 1e-3) / 1e9
-    sel_gbs = sb["select"] / (sel_ms * 1e-3) / 1e9
+    sel_gbs = (sb["append"] + sb["select"]) / (sel_ms * 1e-3) / 1e9
     rect_us = stage_us["rectify"]
     rect_tflops = (rflops / (rect_us * 1e-6) / 1e12) if rect_us else None
     rect_gbs = (rkv / (rect_us * 1e-6) / 1e9) if rect_us else None
@@ -502,9 +552,13 @@ def main():
         "selected_kv_bytes_per_group": sb["selected_kv"] / (w.batch * w.num_kv_heads),
         "full_kv_bytes_per_group": full_cache / (w.batch * w.num_kv_heads),
         "stages_us": {k: (round(v, 2) if v is not None else None) for k, v in stage_us.items()},
-        "select_gbs": round(sel_gbs, 1),
+        "event_pair_us": round(pair_us, 2),
+        "calls_queued_ahead": ahead,
+        "cold_cache_us": {k: round(v, 2) for k, v in cold_us.items()},
+        "cold_decode_gbs": round(sb["decode"] / (cold_us["decode"] * 1e-6) / 1e9, 1),
+        "append_select_gbs": round(sel_gbs, 1),
         "decode_gbs": round(dec_gbs, 1),
-        "sparse_steps_per_s": round(1e6 / (stage_us["append"] + stage_us["select"] + stage_us["decode"]), 1),
+        "sparse_steps_per_s": round(1e6 / (stage_us["append_select"] + stage_us["decode"]), 1),
         "rectify": {"us": rect_us and round(rect_us, 1), "tflops": rect_tflops and round(rect_tflops, 1),
                     "mfma_frac": rect_tflops and round(rect_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                     "gbs": rect_gbs and round(rect_gbs, 1)},

@@ -28,7 +28,7 @@
 // The two kernels hand over through the workspace at the kernel boundary: a
 // cross-workgroup hand-off inside one kernel would need device-scope fences,
 // which write back and invalidate a whole L2 on this multi-die part.
-#include "resa_internal.h"
+#include "refresh_block.h"
 
 namespace resa {
 namespace {
@@ -67,6 +67,11 @@ struct Chunk8<float> {
   }
 };
 
+// Eq. 5's block count with the explicit ratio, in IEEE double.
+__device__ __forceinline__ int select_count(int M, const resa_select_params& p) {
+  return min(M, max(p.n_min, int(ceil(double(M) * p.r))));
+}
+
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double x) {
   const uint64_t u = uint64_t(__double_as_longlong(x));
@@ -86,10 +91,17 @@ __device__ __forceinline__ double row_sum_f64(double x) {
   return x;
 }
 
-// grid: x = chunk of kScoreChunk blocks, y = KV head, z = sequence.
+// grid: x = chunk of kScoreChunk blocks, y = KV head, z = sequence. Only the
+// candidates, blocks below M - min(n_local, n), are scored (the forced newest
+// blocks need no score). With append set, the last x index is not a chunk: its
+// first wave writes the step's new token (k_new / v_new, [B][1][Hkv][D]) at
+// position L - 1 and refreshes that block's descriptor, which no scoring
+// workgroup reads because with n_local >= 1 it is always forced.
 template <typename T, int D>
 __global__ __launch_bounds__(kScoreThreads) void k_score(CacheView c, const void* __restrict__ q,
-                                                         double* __restrict__ scores) {
+                                                         resa_select_params p, double* __restrict__ scores,
+                                                         bool append, const void* __restrict__ k_new,
+                                                         const void* __restrict__ v_new) {
   constexpr int LPB = D / 8;     // lanes per block record (8 channels each)
   constexpr int BPW = 64 / LPB;  // blocks per wave per row of loads
   constexpr int ROWS = kScoreChunk / (4 * BPW);
@@ -97,13 +109,18 @@ __global__ __launch_bounds__(kScoreThreads) void k_score(CacheView c, const void
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int L = c.seq_lens[b];
   const int M = (L + kBlock - 1) / kBlock;
-  if (chunk * kScoreChunk >= M) return;
+  if (append && chunk == int(gridDim.x) - 1) {
+    if (wave == 0 && L > 0) refresh_block<T, D>(c, k_new, v_new, 1, b, g, (L - 1) / kBlock, L, lane);
+    return;
+  }
+  const int Mo = M - min(p.n_local, select_count(M, p));
+  if (chunk * kScoreChunk >= Mo) return;
   const size_t gi = size_t(b) * c.Hkv + g;
   const int sub = lane % LPB, slot = lane / LPB, c0 = sub * 8;
 
   // The group's G query rows (this lane's 8 channels) first, then all page
   // ids, then all descriptor loads, every one issued unconditionally (blocks
-  // past the sequence end re-read block 0) so they are in flight together.
+  // past the candidates re-read block 0) so they are in flight together.
   Chunk8<T> qh[8];
   const size_t qbase = (size_t(b) * c.Hq + size_t(g) * c.G) * D + c0;
 #pragma unroll
@@ -114,7 +131,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_score(CacheView c, const void
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) {
     jr[r] = chunk * kScoreChunk + (r * 4 + wave) * BPW + slot;
-    page[r] = c.bt[size_t(b) * c.maxb + (jr[r] < M ? jr[r] : 0)];
+    page[r] = c.bt[size_t(b) * c.maxb + (jr[r] < Mo ? jr[r] : 0)];
   }
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) {
@@ -137,12 +154,12 @@ __global__ __launch_bounds__(kScoreThreads) void k_score(CacheView c, const void
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) {
     double part = 0.0;
-    if (jr[r] < M) {
+    if (jr[r] < Mo) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) part += qb[e] * double(qb[e] >= 0.0 ? hi[r].get(e) : lo[r].get(e));
     }
     part = row_sum_f64<LPB>(part);
-    if (sub == 0 && jr[r] < M) scores[gi * c.maxb + jr[r]] = part;
+    if (sub == 0 && jr[r] < Mo) scores[gi * c.maxb + jr[r]] = part;
   }
 }
 
@@ -231,7 +248,7 @@ __global__ __launch_bounds__(kTopnThreads) void k_topn(const double* __restrict_
   const int lane = tid & 63, wave = tid >> 6;
   const int L = seq_lens[b];
   const int M = (L + kBlock - 1) / kBlock;
-  const int n = min(M, max(p.n_min, int(ceil(double(M) * p.r))));
+  const int n = select_count(M, p);
   if (g == 0 && tid == 0) count[b] = n;
   const int keep = min(p.n_local, n);
   const int quota = n - keep;
@@ -439,9 +456,10 @@ hipError_t launch_topn(const CacheView& c, const resa_select_params& p, int32_t*
 
 template <typename T, int D>
 hipError_t launch_select_t(const CacheView& c, const void* q, const resa_select_params& p, int32_t* idx,
-                           int32_t* count, int n_cap, double* scores, hipStream_t s) {
-  dim3 g1((c.maxb + kScoreChunk - 1) / kScoreChunk, c.Hkv, c.B);
-  hipLaunchKernelGGL((k_score<T, D>), g1, dim3(kScoreThreads), 0, s, c, q, scores);
+                           int32_t* count, int n_cap, double* scores, bool append, const void* k_new,
+                           const void* v_new, hipStream_t s) {
+  dim3 g1((c.maxb + kScoreChunk - 1) / kScoreChunk + (append ? 1 : 0), c.Hkv, c.B);
+  hipLaunchKernelGGL((k_score<T, D>), g1, dim3(kScoreThreads), 0, s, c, q, p, scores, append, k_new, v_new);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_topn(c, p, idx, count, n_cap, scores, s);
@@ -451,14 +469,34 @@ hipError_t launch_select_t(const CacheView& c, const void* q, const resa_select_
 
 size_t select_ws_bytes(const CacheView& c) { return size_t(c.B) * c.Hkv * c.maxb * sizeof(double); }
 
-hipError_t launch_select(const CacheView& c, const void* q, const resa_select_params& p, int32_t* idx,
-                         int32_t* count, int n_cap, void* ws, hipStream_t s) {
+namespace {
+hipError_t select_dispatch(const CacheView& c, const void* q, const resa_select_params& p, int32_t* idx,
+                           int32_t* count, int n_cap, void* ws, bool append, const void* k_new,
+                           const void* v_new, hipStream_t s) {
   double* scores = static_cast<double*>(ws);
   if (c.dtype == RESA_BF16)
-    return c.D == 128 ? launch_select_t<uint16_t, 128>(c, q, p, idx, count, n_cap, scores, s)
-                      : launch_select_t<uint16_t, 64>(c, q, p, idx, count, n_cap, scores, s);
-  return c.D == 128 ? launch_select_t<float, 128>(c, q, p, idx, count, n_cap, scores, s)
-                    : launch_select_t<float, 64>(c, q, p, idx, count, n_cap, scores, s);
+    return c.D == 128 ? launch_select_t<uint16_t, 128>(c, q, p, idx, count, n_cap, scores, append, k_new, v_new, s)
+                      : launch_select_t<uint16_t, 64>(c, q, p, idx, count, n_cap, scores, append, k_new, v_new, s);
+  return c.D == 128 ? launch_select_t<float, 128>(c, q, p, idx, count, n_cap, scores, append, k_new, v_new, s)
+                    : launch_select_t<float, 64>(c, q, p, idx, count, n_cap, scores, append, k_new, v_new, s);
+}
+}  // namespace
+
+hipError_t launch_select(const CacheView& c, const void* q, const resa_select_params& p, int32_t* idx,
+                         int32_t* count, int n_cap, void* ws, hipStream_t s) {
+  return select_dispatch(c, q, p, idx, count, n_cap, ws, false, nullptr, nullptr, s);
+}
+
+// One decode step's append (n_new = 1) and selection. With n_local >= 1 the
+// newest block is forced, never scored, so its refresh rides in the scoring
+// launch; otherwise the refresh must finish before scoring and runs first.
+hipError_t launch_append_select(const CacheView& c, const void* k_new, const void* v_new, const void* q,
+                                const resa_select_params& p, int32_t* idx, int32_t* count, int n_cap, void* ws,
+                                hipStream_t s) {
+  if (p.n_local >= 1) return select_dispatch(c, q, p, idx, count, n_cap, ws, true, k_new, v_new, s);
+  const hipError_t e = launch_update_tail(c, k_new, v_new, 1, s);
+  if (e != hipSuccess) return e;
+  return launch_select(c, q, p, idx, count, n_cap, ws, s);
 }
 
 }  // namespace resa

@@ -139,6 +139,24 @@ resa_status resa_select_blocks(const resa_cache* cache, const void* q, const res
                     "resa_select_blocks");
 }
 
+resa_status resa_append_select(const resa_cache* cache, const void* k_new, const void* v_new, const void* q,
+                               const resa_select_params* params, int32_t* idx, int32_t* count, int32_t n_cap,
+                               void* ws, size_t ws_bytes, void* stream) {
+  resa::CacheView v;
+  resa_status st = check_cache(cache, &v);
+  if (st != RESA_OK) return st;
+  if ((st = check_params(params)) != RESA_OK) return st;
+  if ((k_new == nullptr) != (v_new == nullptr)) return fail(RESA_ERR_INVALID, "k_new and v_new must both be set or both be NULL");
+  if (!q || !idx || !count) return fail(RESA_ERR_INVALID, "q, idx and count must not be NULL");
+  const int need_cap = n_for((v.max_seq_len + resa::kBlock - 1) / resa::kBlock, params);
+  if (n_cap < need_cap) return fail(RESA_ERR_INVALID, "n_cap %d is below resa_n_cap() = %d", n_cap, need_cap);
+  const size_t need = resa::select_ws_bytes(v);
+  if (!ws || ws_bytes < need) return fail(RESA_ERR_WORKSPACE, "select workspace %zu < %zu bytes", ws_bytes, need);
+  return hip_status(resa::launch_append_select(v, k_new, v_new, q, *params, idx, count, n_cap, ws,
+                                               static_cast<hipStream_t>(stream)),
+                    "resa_append_select");
+}
+
 resa_status resa_sparse_decode(const resa_cache* cache, const void* q, const int32_t* idx,
                                const int32_t* count, int32_t n_cap, float scale, void* out, void* ws,
                                size_t ws_bytes, void* stream) {

@@ -79,6 +79,9 @@ hipError_t launch_rebuild(const CacheView& c, hipStream_t s);
 size_t select_ws_bytes(const CacheView& c);
 hipError_t launch_select(const CacheView& c, const void* q, const resa_select_params& p, int32_t* idx,
                          int32_t* count, int n_cap, void* ws, hipStream_t s);
+hipError_t launch_append_select(const CacheView& c, const void* k_new, const void* v_new, const void* q,
+                                const resa_select_params& p, int32_t* idx, int32_t* count, int n_cap, void* ws,
+                                hipStream_t s);
 
 struct DecodePlan {
   int bps;     // selected blocks per split

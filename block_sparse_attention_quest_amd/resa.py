@@ -22,7 +22,7 @@ _STATUS = {0: "RESA_OK", 1: "RESA_ERR_INVALID", 2: "RESA_ERR_UNSUPPORTED",
            3: "RESA_ERR_WORKSPACE", 4: "RESA_ERR_HIP"}
 EXPORTED = ("resa_n_cap", "resa_select_workspace_size", "resa_decode_workspace_size",
             "resa_rectify_workspace_size", "resa_update_descriptors", "resa_select_blocks",
-            "resa_sparse_decode", "resa_rectify", "resa_last_error")
+            "resa_append_select", "resa_sparse_decode", "resa_rectify", "resa_last_error")
 
 
 class ResaError(RuntimeError):
@@ -67,6 +67,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.resa_update_descriptors.argtypes, lib.resa_update_descriptors.restype = [cp, vp, vp, i32, vp], i32
     lib.resa_select_blocks.argtypes = [cp, vp, pp, vp, vp, i32, vp, sz, vp]
     lib.resa_select_blocks.restype = i32
+    lib.resa_append_select.argtypes = [cp, vp, vp, vp, pp, vp, vp, i32, vp, sz, vp]
+    lib.resa_append_select.restype = i32
     lib.resa_sparse_decode.argtypes = [cp, vp, vp, vp, i32, ctypes.c_float, vp, vp, sz, vp]
     lib.resa_sparse_decode.restype = i32
     lib.resa_rectify.argtypes = [cp, vp, vp, vp, i32, ctypes.c_float, vp, vp, sz, vp]
@@ -180,6 +182,14 @@ def resa_select_blocks(cache: PagedKVCache, q: torch.Tensor, params: ResaSelectP
     _check(load().resa_select_blocks(ctypes.byref(cache.struct), _ptr(q), ctypes.byref(params), _ptr(idx),
                                      _ptr(count), int(n_cap), _ptr(ws), ws.numel() * ws.element_size(),
                                      _stream(stream)))
+
+
+def resa_append_select(cache: PagedKVCache, k_new: Optional[torch.Tensor], v_new: Optional[torch.Tensor],
+                       q: torch.Tensor, params: ResaSelectParams, idx: torch.Tensor, count: torch.Tensor, n_cap: int,
+                       ws: torch.Tensor, stream=None) -> None:
+    _check(load().resa_append_select(ctypes.byref(cache.struct), _ptr(k_new), _ptr(v_new), _ptr(q),
+                                     ctypes.byref(params), _ptr(idx), _ptr(count), int(n_cap), _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def resa_sparse_decode(cache: PagedKVCache, q: torch.Tensor, idx: torch.Tensor, count: torch.Tensor, n_cap: int,

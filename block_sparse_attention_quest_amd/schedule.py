@@ -23,8 +23,12 @@ from . import workloads as W
 
 
 class ResaRunner:
-    def __init__(self, w: W.Workload, device="cuda", steps: Optional[int] = None, inputs_on_device: bool = True):
+    def __init__(self, w: W.Workload, device="cuda", steps: Optional[int] = None, inputs_on_device: bool = True,
+                 fused_append: bool = True):
         self.w = w
+        # one call appends the step's token and selects (resa_append_select)
+        # instead of resa_update_descriptors followed by resa_select_blocks
+        self.fused_append = fused_append
         self.device = device
         self.steps = w.steps if steps is None else steps
         B, Hq, Hkv, d = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim
@@ -96,8 +100,11 @@ class ResaRunner:
         q = si["q"][t] if q is None else q
         k = si["k"][t] if k is None else k
         v = si["v"][t] if v is None else v
-        R.resa_update_descriptors(self.cache, k, v, 1)
-        R.resa_select_blocks(self.cache, q, self.params, self.idx, self.count, self.n_cap, self.ws)
+        if self.fused_append:
+            R.resa_append_select(self.cache, k, v, q, self.params, self.idx, self.count, self.n_cap, self.ws)
+        else:
+            R.resa_update_descriptors(self.cache, k, v, 1)
+            R.resa_select_blocks(self.cache, q, self.params, self.idx, self.count, self.n_cap, self.ws)
         R.resa_sparse_decode(self.cache, q, self.idx, self.count, self.n_cap, self.out, self.ws, self.scale)
         return self.out
 

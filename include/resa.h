@@ -149,6 +149,22 @@ resa_status resa_select_blocks(const resa_cache* cache, const void* q, const res
                                void* stream);
 
 /*
+ * One decode step's cache append and block selection (Pith "What carries the
+ * argument": the newest token's key enters its block's statistics before the
+ * step's selection). The result is exactly that of
+ *   resa_update_descriptors(cache, k_new, v_new, 1, stream);
+ *   resa_select_blocks(cache, q, params, idx, count, n_cap, ws, ws_bytes, stream);
+ * (k_new, v_new: [batch][1][num_kv_heads][head_dim], or both NULL when the cache
+ * already holds the new token). With params->n_local >= 1 the newest block is
+ * always selected and never scored, so the append runs inside the scoring
+ * launch; with n_local == 0 the two run one after the other. Arguments, output
+ * layout, workspace and errors are those of the two calls above.
+ */
+resa_status resa_append_select(const resa_cache* cache, const void* k_new, const void* v_new, const void* q,
+                               const resa_select_params* params, int32_t* idx, int32_t* count, int32_t n_cap,
+                               void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Block-sparse decoding (Eq. 2, Pith referee report minor comment 3): head h of
  * sequence b attends to exactly the valid tokens of the blocks its group g = h / G
  * selected,

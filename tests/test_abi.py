@@ -105,6 +105,28 @@ def test_small_n_cap_and_workspace_are_rejected(lib):
                                   None) == R.RESA_ERR_INVALID
 
 
+def test_append_select_argument_checks(lib):
+    c = _cache()
+    p = R.ResaSelectParams(16, 1, 0.1)
+    buf = ctypes.c_void_p(0xB000)
+    need = lib.resa_select_workspace_size(ctypes.byref(c))
+
+    def call(k=buf, v=buf, q=buf, params=p, n_cap=16, ws_bytes=need, cache=c):
+        return lib.resa_append_select(ctypes.byref(cache) if cache is not None else None, k, v, q,
+                                      ctypes.byref(params), buf, buf, n_cap, buf, ws_bytes, None)
+
+    assert call(cache=None) == R.RESA_ERR_INVALID
+    assert call(cache=_cache(block_size=8)) == R.RESA_ERR_INVALID
+    assert call(v=None) == R.RESA_ERR_INVALID          # k_new without v_new
+    assert call(k=None) == R.RESA_ERR_INVALID
+    assert call(q=None) == R.RESA_ERR_INVALID
+    assert call(params=R.ResaSelectParams(16, -1, 0.1)) == R.RESA_ERR_INVALID
+    assert call(params=R.ResaSelectParams(16, 1, 0.0)) == R.RESA_ERR_INVALID
+    assert call(n_cap=15) == R.RESA_ERR_INVALID
+    assert call(ws_bytes=need - 1) == R.RESA_ERR_WORKSPACE
+    assert lib.resa_last_error()
+
+
 def test_rectify_argument_checks(lib):
     c = _cache()
     buf = ctypes.c_void_p(0xA000)

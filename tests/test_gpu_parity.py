@@ -21,19 +21,20 @@ import parity as P
 pytestmark = pytest.mark.gpu
 
 
-def _runner(w, steps=None):
+def _runner(w, steps=None, fused_append=True):
     from block_sparse_attention_quest_amd.schedule import ResaRunner
     print(f"[case] {w.name} seed={w.seed} B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} d={w.head_dim} "
-          f"prefill={w.prefill_lens[:4]} steps={w.steps if steps is None else steps} f={w.f}", flush=True)
-    r = ResaRunner(w, steps=steps)
+          f"prefill={w.prefill_lens[:4]} steps={w.steps if steps is None else steps} f={w.f} "
+          f"fused_append={fused_append}", flush=True)
+    r = ResaRunner(w, steps=steps, fused_append=fused_append)
     r.fill_prefill()
     r.build_descriptors()
     return r
 
 
-def _run_loop_parity(w, steps=None, check_all_desc_every=0):
+def _run_loop_parity(w, steps=None, check_all_desc_every=0, fused_append=True):
     steps = w.steps if steps is None else steps
-    r = _runner(w, steps)
+    r = _runner(w, steps, fused_append)
     oc = P.oracle_cache(w)
     torch.cuda.synchronize()
     P.assert_desc_equal(r.cache.desc, oc)
@@ -101,6 +102,35 @@ def test_small_schedules(case):
     w = W.Workload(name, dt, B, Hq, Hkv, d, pre, steps, f, n_min, r, n_local,
                    tuple(max(0, min(3, (L // 16) - 1)) for L in pre), dt == "bf16", 100 + len(name))
     _run_loop_parity(w)
+
+
+@pytest.mark.parametrize("case", [SMALL[0], SMALL[7]], ids=["bf16_g4_d128", "bf16_no_local"])
+def test_small_schedules_unfused_append(case):
+    """The same schedules with the append as its own call (resa_update_descriptors)
+    before resa_select_blocks."""
+    name, dt, B, Hq, Hkv, d, pre, steps, f, n_min, r, n_local = case
+    w = W.Workload(name, dt, B, Hq, Hkv, d, pre, steps, f, n_min, r, n_local,
+                   tuple(max(0, min(3, (L // 16) - 1)) for L in pre), dt == "bf16", 100 + len(name))
+    _run_loop_parity(w, fused_append=False)
+
+
+def test_fused_and_unfused_append_agree():
+    """resa_append_select leaves the cache, descriptors, selection and output
+    exactly as resa_update_descriptors + resa_select_blocks do."""
+    w = W.Workload("fused_vs_unfused", "bf16", 3, 16, 4, 128, (15, 513, 3000), 20, 0, 8, 0.1, 2,
+                   (0, 2, 3), True, 31)
+    a, b = _runner(w, fused_append=True), _runner(w, fused_append=False)
+    for t in range(w.steps):
+        oa, ob = a.decode_step(t), b.decode_step(t)
+        torch.cuda.synchronize()
+        assert torch.equal(a.count, b.count), t
+        for s in range(w.batch):
+            n = int(a.count[s])
+            assert torch.equal(a.idx[s, :, :n], b.idx[s, :, :n]), (t, s)
+        assert torch.equal(oa, ob), t
+    assert torch.equal(a.cache.desc, b.cache.desc)
+    assert torch.equal(a.cache.k_pages, b.cache.k_pages)
+    assert torch.equal(a.cache.v_pages, b.cache.v_pages)
 
 
 def test_single_token_sequences():
