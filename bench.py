@@ -542,7 +542,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "prefill": w.prefill_lens[0], "q_heads": w.num_q_heads,
                    "kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block": 16, "r": w.r, "n_min": w.n_min,
                    "n_local": w.n_local, "f": w.f, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "resa_sparse_decode (k_decode + k_decode_combine)",
+        "roofline": {"bound": "hbm", "kernel": "resa_sparse_decode (k_decode_mfma + k_decode_combine)",
                      "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": decode_traffic(w),
                      "alg_bytes_per_launch": sb["decode"], "avg_launch_us": round(dec_ms * 1e3, 2)},

@@ -3,29 +3,23 @@
 // its 16-token block is selected), split over the key axis in the manner of
 // Flash-Decoding (reference [6] of the Pith reference list), then merged exactly.
 //
-// k_decode, grid (split, KV head, sequence), 4 waves. A split is a run of the
-// group's selected blocks; wave w takes every 4th of them. Per block the wave
-// reads the K tile (16 tokens x d, token-major) and the V tile (stored
-// channel-major, d x 16 tokens) of one page, 4 KiB each at d = 128 bf16, and
-// serves all G query heads of the group from them, so each selected byte is
-// fetched once per group. Two blocks ahead are in flight while one is
-// processed (three rotating register sets, so no copy ever waits on a load).
-//   q.k: lane = 8 * tp + cg holds tokens tp and tp + 8 and channels
-//   cg*8 + 64*k + [0, 8) of K (every 16-byte load covers whole 128-byte lines);
-//   bf16 pairs go through v_dot2 with fp32 accumulation, then a 3-step DPP sum
-//   over the 8 lanes that share the tokens.
-//   softmax: one running max per head for the whole wave, moved only when a
-//   logit exceeds it by more than 2^8 (numerator and denominator share every
-//   rescale, so the result is unchanged); each of the 2G (token, head) pairs of
-//   a token pair is exponentiated by one lane and published through LDS.
-//   p.V: lane owns head_dim/64 channels; its V rows are 16 contiguous tokens,
-//   so with bf16 the probabilities are rounded to bf16 and multiplied in token
-//   pairs with v_dot2 (fp32 accumulation; the softmax denominator sums the
-//   same rounded values).
-// The 4 wave states are merged through LDS into one split partial (m, l,
-// acc[d]) in fp32; k_decode_combine then merges a group's splits with
-// log-sum-exp weights (a separate kernel, so the hand-off needs no
-// device-scope fence).
+// grid (split, KV head, sequence), 4 waves. A split is a run of the group's
+// selected blocks; wave w takes every 4th of them. Per block the wave reads the
+// K tile (16 tokens x d, token-major) and the V tile (stored channel-major,
+// d x 16 tokens) of one page, 4 KiB each at d = 128 bf16, and serves all G
+// query heads of the group from them, so each selected byte is fetched once per
+// group. The next blocks are in flight while one is processed (rotating
+// register sets, so no copy ever waits on a load). The softmax keeps one running
+// max per head, moved only when a logit exceeds it by more than 2^8 (numerator
+// and denominator share every rescale, so the result is unchanged). The 4 wave
+// states are merged through LDS into one split partial (m, l, acc[d]) in fp32;
+// k_decode_combine then merges a group's splits with log-sum-exp weights (a
+// separate kernel, so the hand-off needs no device-scope fence).
+//
+// k_decode_mfma (bf16 cache) runs both products on the matrix cores; k_decode
+// (fp32 cache) on the VALU.
+#include <type_traits>
+
 #include "resa_internal.h"
 
 namespace resa {
@@ -34,19 +28,11 @@ namespace {
 constexpr float kLazyRescale = 8.0f;  // log2 units
 constexpr int kDecWaves = 4;
 constexpr int kDecThreads = 64 * kDecWaves;
+constexpr int kDecBuffers = 3;   // blocks per wave in registers: one in use, the rest loading
 
 // One lane's channels of one K token row.
 template <typename T, int D>
 struct KRow;
-template <int D>
-struct KRow<uint16_t, D> {
-  static constexpr int NCH = D / 64;
-  uint4 u[NCH];
-  __device__ void load(const uint16_t* row, int cg) {
-#pragma unroll
-    for (int k = 0; k < NCH; ++k) u[k] = *reinterpret_cast<const uint4*>(row + cg * 8 + 64 * k);
-  }
-};
 template <int D>
 struct KRow<float, D> {
   static constexpr int NCH = D / 64;
@@ -69,30 +55,6 @@ struct KRow<float, D> {
 // The query of one head restricted to the lane's K channels.
 template <typename T, int D>
 struct QRow;
-template <int D>
-struct QRow<uint16_t, D> {
-  static constexpr int NCH = D / 64;
-  uint32_t w[NCH * 4];
-  __device__ void load(const uint16_t* row, int cg) {
-#pragma unroll
-    for (int k = 0; k < NCH; ++k) {
-      const uint4 u = *reinterpret_cast<const uint4*>(row + cg * 8 + 64 * k);
-      w[4 * k + 0] = u.x; w[4 * k + 1] = u.y; w[4 * k + 2] = u.z; w[4 * k + 3] = u.w;
-    }
-  }
-  __device__ float dot(const KRow<uint16_t, D>& kr) const {
-    float s = 0.f;
-#pragma unroll
-    for (int k = 0; k < NCH; ++k) {
-      const uint32_t kk[4] = {kr.u[k].x, kr.u[k].y, kr.u[k].z, kr.u[k].w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[4 * k + i]),
-                                            __builtin_bit_cast(bf16x2_t, kk[i]), s, false);
-    }
-    return s;
-  }
-};
 template <int D>
 struct QRow<float, D> {
   static constexpr int NC = D / 8;
@@ -117,39 +79,6 @@ struct QRow<float, D> {
 // One lane's V rows (channel-major page tile): CPL channels x 16 tokens.
 template <typename T, int CPL>
 struct VRows;
-template <int CPL>
-struct VRows<uint16_t, CPL> {
-  uint4 u[CPL][2];  // 16 bf16 tokens per channel
-  __device__ void load(const uint16_t* tile, int lane) {
-#pragma unroll
-    for (int cc = 0; cc < CPL; ++cc) {
-      const uint4* p = reinterpret_cast<const uint4*>(tile + (lane * CPL + cc) * 16);
-      u[cc][0] = p[0];
-      u[cc][1] = p[1];
-    }
-  }
-  __device__ float get(int cc, int t) const {
-    const uint4 w = u[cc][t / 8];
-    const int r = (t % 8) / 2;
-    const uint32_t x = r == 0 ? w.x : r == 1 ? w.y : r == 2 ? w.z : w.w;
-    return (t & 1) ? bf16_hi(x) : bf16_lo(x);
-  }
-  __device__ static uint32_t keep2(uint32_t x, int t0, int valid) {
-    return x & ((t0 < valid ? 0x0000ffffu : 0u) | (t0 + 1 < valid ? 0xffff0000u : 0u));
-  }
-  __device__ void mask_tokens(int valid) {
-#pragma unroll
-    for (int cc = 0; cc < CPL; ++cc)
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        uint4& w = u[cc][i];
-        w.x = keep2(w.x, 8 * i + 0, valid);
-        w.y = keep2(w.y, 8 * i + 2, valid);
-        w.z = keep2(w.z, 8 * i + 4, valid);
-        w.w = keep2(w.w, 8 * i + 6, valid);
-      }
-  }
-};
 template <int CPL>
 struct VRows<float, CPL> {
   float4 u[CPL][4];
@@ -197,13 +126,16 @@ __device__ __forceinline__ void store_out(void* out, size_t i, float x) {
   else static_cast<float*>(out)[i] = x;
 }
 
+// The wave states of a split, merged into its partial.
 template <int G, int D>
-struct DecSmem {
-  float p[kDecWaves][16][G];       // fp32 cache: probabilities of the current block
-  uint16_t pb[kDecWaves][G][16];   // bf16 cache: the same, rounded, token pairs adjacent
+struct DecMerge {
   float m[kDecWaves][G];
   float l[kDecWaves][G];
   float acc[kDecWaves][G][D];
+};
+template <int G, int D>
+struct DecSmem : DecMerge<G, D> {
+  float p[kDecWaves][16][G];       // probabilities of the current block
 };
 
 // The K rows (tokens tp, tp + 8) and V rows of one block for one lane.
@@ -218,13 +150,19 @@ struct BlockRegs {
   }
 };
 
-// grid: x = split, y = KV head, z = sequence; 256 threads.
+// fp32 cache, VALU. grid: x = split, y = KV head, z = sequence; 256 threads.
+//   q.k: lane = 8 * tp + cg holds tokens tp and tp + 8 and channels
+//   cg*8 + 64*k + [0, 8) of K; fp32 FMAs, then a 3-step DPP sum over the 8 lanes
+//   that share the tokens.
+//   softmax: each of the 2G (token, head) pairs of a token pair is
+//   exponentiated by one lane and published through LDS.
+//   p.V: lane owns head_dim/64 channels; its V rows are 16 contiguous tokens.
 template <typename T, int D, int G>
 __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
+  static_assert(sizeof(T) == 4, "the bf16 cache decodes on the matrix cores");
   constexpr int CPL = D / 64;                      // V channels per lane
   constexpr int PAIRS = 2 * G;                     // (token, head) pairs per token pair
   constexpr int PPL = PAIRS > 8 ? PAIRS / 8 : 1;   // pairs per lane
-  constexpr bool BF16 = sizeof(T) == 2;
   __shared__ DecSmem<G, D> sm;
   const CacheView& c = a.c;
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -325,40 +263,15 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
           }
         const float pf = x == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(x - mh);
         const int t = second ? tp + 8 : tp;
-        if constexpr (BF16) {
-          const uint16_t pbits = f32_to_bf16(pf);  // the value p.V uses; l sums the same value
-          lpart[u] += bf16_to_f32(pbits);
-          sm.pb[wave][h][t] = pbits;
-        } else {
-          lpart[u] += pf;
-          sm.p[wave][t][h] = pf;
-        }
+        lpart[u] += pf;
+        sm.p[wave][t][h] = pf;
       }
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     if (valid < kBlock) cur.v.mask_tokens(valid);  // slots past the sequence end may hold anything
-    if constexpr (BF16) {
-      // p.V as bf16 pair dot products: a V row word holds tokens (2i, 2i + 1)
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const uint4* pp = reinterpret_cast<const uint4*>(&sm.pb[wave][h][0]);
-        const uint4 p03 = pp[0], p47 = pp[1];
-        const uint32_t pw[8] = {p03.x, p03.y, p03.z, p03.w, p47.x, p47.y, p47.z, p47.w};
-#pragma unroll
-        for (int cc = 0; cc < CPL; ++cc) {
-          const uint32_t vw[8] = {cur.v.u[cc][0].x, cur.v.u[cc][0].y, cur.v.u[cc][0].z, cur.v.u[cc][0].w,
-                                  cur.v.u[cc][1].x, cur.v.u[cc][1].y, cur.v.u[cc][1].z, cur.v.u[cc][1].w};
-          float sacc = acc[h][cc];
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-            sacc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[i]),
-                                                   __builtin_bit_cast(bf16x2_t, vw[i]), sacc, false);
-          acc[h][cc] = sacc;
-        }
-      }
-    } else {
+    {
 #pragma unroll
       for (int t = 0; t < kBlock; ++t) {
         float pt[G];
@@ -426,6 +339,200 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
     if (ch == 0) {
       a.part_ml[(part * G + h) * 2 + 0] = mx;
       a.part_ml[(part * G + h) * 2 + 1] = den;
+    }
+  }
+}
+
+// bf16 cache: the same split and wave structure with both products on the
+// matrix cores. Per block a wave computes S^T = K Q^T with D/32 MFMAs
+// 16x16x32 (A: the K tile, lane l holding token l % 16 and channels
+// 32 ks + 8 (l / 16) + [0, 8); B: the group's queries in the same channel order,
+// lane l holding head l % 16, zero for l % 16 >= G). The result leaves lane l
+// with head l % 16 and tokens 4 (l / 16) + [0, 4), which is exactly where the
+// B operand of a 16x16x16 MFMA wants P^T, so after the online softmax the
+// probabilities (rounded to bf16; the denominator sums the same rounded values)
+// go straight into O^T += V^T P^T, D/16 MFMAs whose A operands are 8-byte
+// pieces of the channel-major V tile (lane l: channel 16 dt + l % 16, tokens
+// 4 (l / 16) + [0, 4)). A lane keeps the running max, denominator and O^T
+// column of one head: no cross-lane sums, one max over the four lane groups
+// per block.
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <int D>
+struct MfmaBlock {
+  uint4 k[D / 32];  // S^T A operand pieces
+  uint2 v[D / 16];  // O^T A operand pieces
+  __device__ void load(const uint16_t* kt, const uint16_t* vt, int lane) {
+    const int t = lane & 15, j = lane >> 4;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) k[ks] = *reinterpret_cast<const uint4*>(kt + t * D + 32 * ks + 8 * j);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) v[dt] = *reinterpret_cast<const uint2*>(vt + (16 * dt + t) * kBlock + 4 * j);
+  }
+};
+
+// grid: x = split, y = KV head, z = sequence; 256 threads.
+template <int D, int G, int NB>
+__global__ __launch_bounds__(kDecThreads) void k_decode_mfma(DecodeArgs a) {
+  constexpr int KS = D / 32, DT = D / 16;
+  __shared__ DecMerge<G, D> sm;
+  const CacheView& c = a.c;
+  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane & 15, j = lane >> 4;  // head column, token group
+  const size_t gi = size_t(b) * c.Hkv + g;
+  const int first = s * a.bps;
+
+  // block and page ids of this wave's blocks (first + wave + 4 i), clamped
+  // into their rows so every load is in bounds; as in the VALU kernel
+  int my_blk = 0, my_page = 0;
+  if (lane * kDecWaves < a.bps) {
+    const int pos = min(first + wave + kDecWaves * lane, a.n_cap - 1);
+    my_blk = min(max(a.idx[gi * a.n_cap + pos], 0), c.maxb - 1);
+    my_page = min(max(c.bt[size_t(b) * c.maxb + my_blk], 0), c.num_pages - 1);
+  }
+  const int n = a.count[b];
+  const int L = c.seq_lens[b];
+  uint4 qk[KS];
+  {
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (size_t(b) * c.Hq + size_t(g) * G + (h < G ? h : 0)) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint4 x = *reinterpret_cast<const uint4*>(qrow + 32 * ks + 8 * j);
+      qk[ks] = h < G ? x : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  const uint16_t* kbase = static_cast<const uint16_t*>(c.k);
+  const uint16_t* vbase = static_cast<const uint16_t*>(c.v);
+  auto tile = [&](const uint16_t* base, int page) { return base + (size_t(page) * c.Hkv + g) * kBlock * D; };
+  // NB rotating buffers: block it in one, blocks it + 1 .. it + NB - 1 loading
+  MfmaBlock<D> buf[NB];
+#pragma unroll
+  for (int u = 0; u < NB - 1; ++u) {
+    const int pu = __builtin_amdgcn_readlane(my_page, u);
+    buf[u].load(tile(kbase, pu), tile(vbase, pu), lane);
+  }
+  const int nblk = min(a.bps, n - first);
+  if (nblk <= 0) return;
+  const int nw = nblk > wave ? (nblk - wave + kDecWaves - 1) / kDecWaves : 0;
+
+  float m = -__builtin_inff(), lsum = 0.f;
+  f32x4_t o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const uint32_t ones = 0x3F803F80u;  // bf16 pair (1, 1)
+
+  auto step = [&](int it, MfmaBlock<D>& cur, MfmaBlock<D>& spare) {
+    if (it + NB - 1 < nw) {
+      const int np = __builtin_amdgcn_readlane(my_page, it + NB - 1);
+      spare.load(tile(kbase, np), tile(vbase, np), lane);
+    }
+    const int blk = __builtin_amdgcn_readlane(my_blk, it);
+    const int valid = min(kBlock, L - blk * kBlock);
+    f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur.k[ks]),
+                                                    __builtin_bit_cast(bf16x8_t, qk[ks]), sc, 0, 0, 0);
+    if (valid < kBlock) {  // wave-uniform: slots past the sequence end may hold anything
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (4 * j + r >= valid) sc[r] = -__builtin_inff();
+      const uint32_t m0 = (4 * j + 0 < valid ? 0x0000ffffu : 0u) | (4 * j + 1 < valid ? 0xffff0000u : 0u);
+      const uint32_t m1 = (4 * j + 2 < valid ? 0x0000ffffu : 0u) | (4 * j + 3 < valid ? 0xffff0000u : 0u);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        cur.v[dt].x &= m0;
+        cur.v[dt].y &= m1;
+      }
+    }
+    float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])) * a.scale_log2;
+    bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+    bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+    // the running max moves only on a jump of more than 2^8; numerator and
+    // denominator share every rescale
+    if (__builtin_amdgcn_ballot_w64(bm > m + kLazyRescale)) {
+      if (bm > m + kLazyRescale) {
+        const float alpha = m == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m - bm);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+        lsum *= alpha;
+        m = bm;
+      }
+    }
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      p[r] = sc[r] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(fmaf(sc[r], a.scale_log2, -m));
+    const f32x2_t p01 = {p[0], p[1]}, p23 = {p[2], p[3]};
+    const uint32_t w01 = __builtin_bit_cast(uint32_t, __builtin_convertvector(p01, bf16x2_t));
+    const uint32_t w23 = __builtin_bit_cast(uint32_t, __builtin_convertvector(p23, bf16x2_t));
+    lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w01), __builtin_bit_cast(bf16x2_t, ones), lsum,
+                                           false);
+    lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w23), __builtin_bit_cast(bf16x2_t, ones), lsum,
+                                           false);
+    const s16x4_t pb = __builtin_bit_cast(s16x4_t, make_uint2(w01, w23));
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, cur.v[dt]), pb, o[dt], 0, 0, 0);
+  };
+
+  for (int it0 = 0; it0 < nw; it0 += NB) {
+    bool done = false;
+    static_for<0, NB>([&](auto U) {
+      constexpr int u = U.value;
+      if (!done) {
+        if (it0 + u >= nw) {
+          done = true;
+        } else {
+          step(it0 + u, buf[u], buf[(u + NB - 1) % NB]);
+        }
+      }
+    });
+  }
+
+  // wave state -> LDS: lane (h, j) holds O^T rows 16 dt + 4 j + r of head h
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+  if (h < G) {
+    if (j == 0) {
+      sm.m[wave][h] = nw > 0 ? m : -__builtin_inff();
+      sm.l[wave][h] = nw > 0 ? lsum : 0.f;
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sm.acc[wave][h][16 * dt + 4 * j + r] = o[dt][r];
+  }
+  __syncthreads();
+  const size_t part = gi * a.splits + s;
+  for (int i = tid; i < G * D; i += kDecThreads) {
+    const int hh = i / D, ch = i % D;
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) mx = fmaxf(mx, sm.m[w][hh]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) {
+      const float mw = sm.m[w][hh];
+      const float e = mw == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(mw - mx);
+      num = fmaf(e, sm.acc[w][hh][ch], num);
+      den = fmaf(e, sm.l[w][hh], den);
+    }
+    a.part_acc[(part * G + hh) * D + ch] = num;
+    if (ch == 0) {
+      a.part_ml[(part * G + hh) * 2 + 0] = mx;
+      a.part_ml[(part * G + hh) * 2 + 1] = den;
     }
   }
 }
@@ -500,7 +607,10 @@ template <typename T, int D, int G>
 hipError_t launch_decode_t(const DecodeArgs& a, void* out, hipStream_t st) {
   const CacheView& c = a.c;
   dim3 grid(a.splits, c.Hkv, c.B);
-  hipLaunchKernelGGL((k_decode<T, D, G>), grid, dim3(kDecThreads), 0, st, a);
+  if constexpr (sizeof(T) == 2)
+    hipLaunchKernelGGL((k_decode_mfma<D, G, kDecBuffers>), grid, dim3(kDecThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_decode<float, D, G>), grid, dim3(kDecThreads), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 g2(c.Hkv, c.B, G);
