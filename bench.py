@@ -268,12 +268,19 @@ def sweep(args):
     stream = torch.cuda.current_stream()
 
     def timed(fn, n):
+        """GPU time per call of n calls queued back to back behind a spin kernel
+        (so the host's per-call cost does not enter at batch 1)."""
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
+        torch.cuda._sleep(QUEUE_AHEAD_CYCLES)
+        held = torch.cuda.Event()
+        held.record(stream)
         e0.record(stream)
         for i in range(n):
             fn(i)
         e1.record(stream)
+        if held.query():
+            print("[sweep] warning: the GPU caught up with the host while calls were queued", file=sys.stderr)
         torch.cuda.synchronize()
         return 1e3 * e0.elapsed_time(e1) / n
 
