@@ -540,66 +540,73 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_mfma(DecodeArgs a) {
 // grid: x = KV head, y = sequence; 256 threads: merge a group's splits. Each
 // thread owns (head, channel) outputs; the partials of up to 16 splits are
 // requested in one batch before any is used, merged with log-sum-exp weights.
-constexpr int kMaxSplits = 512;  // plan_decode keeps splits at or below this
 constexpr int kCombThreads = 256;
 
-// Sum (SUM) or maximum over the workgroup; every thread gets the result.
-template <bool SUM>
-__device__ __forceinline__ float block_reduce(float x, float* red) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const float y = __shfl_xor(x, o, 64);
-    x = SUM ? x + y : fmaxf(x, y);
-  }
-  if (lane == 0) red[wave] = x;
-  __syncthreads();
-  x = red[0];
-#pragma unroll
-  for (int w = 1; w < kCombThreads / 64; ++w) x = SUM ? x + red[w] : fmaxf(x, red[w]);
-  __syncthreads();
-  return x;
-}
-
 // Merge the splits of one query head: grid (KV head, sequence, head of the
-// group), 256 threads. The splits' maxima and log-sum-exp weights come first
-// (threads over splits), then thread (part, channel) accumulates every
-// (256 / D)-th split's partial of its channel with all loads independent, and
-// the parts are summed in LDS.
+// group), 256 threads. Thread (part, channel) folds every (256 / D)-th split
+// of its channel into a running (max, numerator, denominator), requesting the
+// splits' (m, l) and partials in batches of 16 before any is used, so a batch
+// costs one round trip; the parts are then merged through LDS with the same
+// log-sum-exp weights.
 template <typename T, int D, int G>
 __global__ __launch_bounds__(kCombThreads) void k_decode_combine(DecodeArgs a, void* __restrict__ out) {
   constexpr int PARTS = kCombThreads / D;
-  __shared__ float w[kMaxSplits];
-  __shared__ float red[kCombThreads / 64];
-  __shared__ float part_num[PARTS][D];
+  constexpr int BATCH = 16;
+  __shared__ float pm[PARTS][D], pnum[PARTS][D], pden[PARTS][D];
   const CacheView& c = a.c;
   const int g = blockIdx.x, b = blockIdx.y, h = blockIdx.z, tid = threadIdx.x;
   const size_t gi = size_t(b) * c.Hkv + g;
   const int live = (a.count[b] + a.bps - 1) / a.bps;
-  const float* ml = a.part_ml + (gi * a.splits * G + h) * 2;  // split sp at ml[sp * G * 2]
-  float mx = -__builtin_inff();
-  for (int sp = tid; sp < live; sp += kCombThreads) mx = fmaxf(mx, ml[sp * G * 2]);
-  mx = block_reduce<false>(mx, red);
-  float den = 0.f;
-  for (int sp = tid; sp < live; sp += kCombThreads) {
-    const float m = ml[sp * G * 2];
-    const float e = m == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m - mx);
-    w[sp] = e;
-    den = fmaf(e, ml[sp * G * 2 + 1], den);
-  }
-  den = block_reduce<true>(den, red);  // its barriers also publish w
-  const int ch = tid % D, part = tid / D;
+  const int ch = tid % D, part = tid / D;  // part is wave-uniform
+  const float* ml = a.part_ml + (gi * a.splits * G + h) * 2;         // split sp at ml[sp * G * 2]
   const float* acc = a.part_acc + (gi * a.splits * G + h) * D + ch;  // split sp at acc[sp * G * D]
-  float num = 0.f;
-#pragma unroll 16
-  for (int sp = part; sp < live; sp += PARTS) num = fmaf(w[sp], acc[size_t(sp) * G * D], num);
-  part_num[part][ch] = num;
+  float mx = -__builtin_inff(), num = 0.f, den = 0.f;
+  for (int sp0 = part; sp0 < live; sp0 += PARTS * BATCH) {
+    float mv[BATCH], lv[BATCH], av[BATCH];
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const int sp = sp0 + u * PARTS;
+      const int sc = sp < live ? sp : part;  // past the live splits: re-read this part's first
+      mv[u] = ml[size_t(sc) * G * 2];
+      lv[u] = ml[size_t(sc) * G * 2 + 1];
+      av[u] = acc[size_t(sc) * G * D];
+    }
+    // the batch's maximum first, one rescale, then independent weights
+    float bm = -__builtin_inff();
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      if (sp0 + u * PARTS >= live) mv[u] = -__builtin_inff();
+      bm = fmaxf(bm, mv[u]);
+    }
+    if (bm > mx) {  // wave-uniform
+      const float sc = mx == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(mx - bm);
+      num *= sc;
+      den *= sc;
+      mx = bm;
+    }
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const float e = mv[u] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(mv[u] - mx);
+      num = fmaf(e, av[u], num);
+      den = fmaf(e, lv[u], den);
+    }
+  }
+  pm[part][ch] = mx;
+  pnum[part][ch] = num;
+  pden[part][ch] = den;
   __syncthreads();
   if (part == 0) {
-    float t = part_num[0][ch];
+    float m = pm[0][ch];
 #pragma unroll
-    for (int q = 1; q < PARTS; ++q) t += part_num[q][ch];
-    store_out<T>(out, (size_t(b) * c.Hq + size_t(g) * G + h) * D + ch, t / den);
+    for (int q = 1; q < PARTS; ++q) m = fmaxf(m, pm[q][ch]);
+    float t = 0.f, d = 0.f;
+#pragma unroll
+    for (int q = 0; q < PARTS; ++q) {
+      const float e = pm[q][ch] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(pm[q][ch] - m);
+      t = fmaf(e, pnum[q][ch], t);
+      d = fmaf(e, pden[q][ch], d);
+    }
+    store_out<T>(out, (size_t(b) * c.Hq + size_t(g) * G + h) * D + ch, t / d);
   }
 }
 
@@ -638,7 +645,7 @@ DecodePlan plan_decode(const CacheView& c, int n_cap) {
   bps = bps < 4 ? 4 : (bps > 256 ? 256 : bps);
   DecodePlan p;
   p.bps = bps;
-  p.splits = (n_cap + bps - 1) / bps;  // <= 512 (kMaxSplits): bps >= ceil(work / 512) >= n_cap / 512
+  p.splits = (n_cap + bps - 1) / bps;  // <= 512: bps >= ceil(work / 512) >= n_cap / 512
   return p;
 }
 
