@@ -356,6 +356,8 @@ def main():
     ap.add_argument("--workload", default="gqa_128k")
     ap.add_argument("--sweep", action="store_true",
                     help="context-length sweep at batch 1: dense / sparse / rectify breakdown (not the bench line)")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay the timed steps from one HIP graph (no per-launch host work)")
     ap.add_argument("--unfused-append", action="store_true",
                     help="append with resa_update_descriptors, then resa_select_blocks (two calls)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -445,16 +447,26 @@ def main():
             if ev is not None:
                 ev[7].record(stream)
 
-    # ---- timed region: K whole steps; events only at its two ends ----
+    # ---- timed region: K whole steps; events only at its two ends. With
+    # --graph the K steps are recorded into one HIP graph first (recording runs
+    # nothing) and the timed region is its replay ----
+    graph = None
+    if args.graph:
+        graph, _, _ = r.capture(Wu, Wu + K, {t: x for t, x in rect_in.items() if Wu <= t < Wu + K})
+        torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
-    for i in range(K):
-        step_calls(Wu + i)
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(K):
+            step_calls(Wu + i)
     e1.record(stream)
     torch.cuda.synchronize()
     total_ms = e0.elapsed_time(e1)
     ms_per_step = total_ms / K
+    del graph
 
     # ---- per-call durations: MEASURE_STEPS more steps, HIP events around every
     # call on the launch stream, queued without per-step synchronisation ----
@@ -546,6 +558,7 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
+        "launch": "one HIP graph of the timed steps" if args.graph else "calls from the host, one by one",
         "config": {"workload": w.name, "batch": w.batch, "prefill": w.prefill_lens[0], "q_heads": w.num_q_heads,
                    "kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block": 16, "r": w.r, "n_min": w.n_min,
                    "n_local": w.n_local, "f": w.f, "parallelism": "single GPU"},

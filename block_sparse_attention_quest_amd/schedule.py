@@ -142,6 +142,33 @@ class ResaRunner:
             self.rect_inputs[t] = tuple(x.to(self.device) for x in W.rectify_inputs(self.w, t))
         return self.rect_inputs[t]
 
+    def capture(self, t0: int, t1: int, rect_in: Optional[Dict[int, tuple]] = None,
+                keep_outputs: bool = False):
+        """Record decode steps t0 .. t1-1 (and, from `rect_in`, the
+        rectification after each step listed there) into one HIP graph, so a
+        replay issues them with no per-launch host work. Every call in the
+        steps launches kernels only (no allocation, no memset), so the graph
+        replays them exactly. With keep_outputs each step's output (and each
+        rectification's) is also copied into a buffer of its own inside the
+        graph; returns (graph, step outputs, rectify outputs)."""
+        rect_in = rect_in or {}
+        outs = torch.empty(t1 - t0, *self.out.shape, dtype=self.out.dtype, device=self.device) if keep_outputs else None
+        routs: Dict[int, torch.Tensor] = {}
+        stream = torch.cuda.Stream()
+        stream.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for t in range(t0, t1):
+                o = self.decode_step(t)
+                if keep_outputs:
+                    outs[t - t0].copy_(o)
+                if t in rect_in:
+                    ro = self.rectify(t, *rect_in[t])
+                    if keep_outputs:
+                        routs[t] = ro.clone()
+        torch.cuda.current_stream().wait_stream(stream)
+        return graph, outs, routs
+
     def run(self, steps: Optional[int] = None, on_step=None, on_rectify=None) -> None:
         """The full schedule: every step, then a rectification after each f-th."""
         steps = self.steps if steps is None else steps
