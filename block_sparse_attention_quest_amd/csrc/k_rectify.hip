@@ -6,11 +6,13 @@
 //
 // bf16 path (k_rect_mfma): per KV head the G * f query rows form one dense
 // contraction against every key, so it runs on the matrix cores
-// (v_mfma_f32_32x32x16_bf16). The keys of all (sequence, KV head) pairs, laid
-// end to end in tiles of 32, are cut into one equal range per workgroup (the
-// work plan, k_rect_plan), so a mixed-length batch still fills the chip evenly;
-// a range that crosses from one (sequence, KV head) into the next becomes two
-// work items with a partial each. For an item the K/V tiles stream from HBM
+// (v_mfma_f32_32x32x16_bf16). The rows are cut into row tiles of 128 or 256
+// (one wave per 32 rows); a row tile needs the keys up to the last position its
+// last row sees. The key ranges of all (sequence, KV head, row tile) segments,
+// laid end to end in tiles of 32 keys, are cut into one equal range per
+// workgroup (the work plan, k_rect_plan), so a mixed-length batch still fills
+// the chip evenly; a range that crosses from one segment into the next becomes
+// two work items with a partial each. For an item the K/V tiles stream from HBM
 // into LDS once and serve all G * f rows (HBM traffic is the cache once per
 // event, not once per head). Each wave owns a 32-row tile of queries, kept in
 // registers. Scores are computed transposed, S^T = K Q^T, so a lane holds 16
@@ -38,11 +40,13 @@ struct RectArgs {
   CacheView c;
   const void* q;  // [B][f][Hq][D]
   int f, rows, rows_pad;
+  int tile_rows;  // rows per row tile (32 per wave of the launch)
+  int rtiles;     // row tiles per (sequence, KV head)
   int target;     // workgroups aimed for: one round over the chip
   int slots;      // workgroups launched (>= what any plan uses)
   float scale_log2;
-  int4* items;    // [slots + B * Hkv] (sequence, KV head, first key, end key)
-  int2* groups;   // [B * Hkv] (first item, item count) of every (sequence, KV head)
+  int4* items;    // [slots + B * Hkv * rtiles] (sequence, KV head | row tile << 16, first key, end key)
+  int2* groups;   // [B * Hkv * rtiles] (first item, item count) of every segment
   int* wg_first;  // [slots + 1] first item of every workgroup; the rest are nitems
   long long* ptile;  // [B] key tiles of the sequences before each one
   float* part_ml;   // [items][rows_pad][2]
@@ -76,9 +80,11 @@ __device__ long long block_exclusive_scan(long long v, long long* sh, long long*
 }
 
 // Work plan of one rectification, built on the device from seq_lens.
-// Segment s = (sequence b, KV head g) covers T_b = ceil(L_b / 32) key tiles;
-// segments in order (b, then g) make one line of TT tiles, split into P equal
-// workgroup ranges at lo(w) = floor(w TT / P). P is the fewest whole rounds
+// Segment s = (sequence b, KV head g, row tile rt) covers the key tiles up to
+// the last position its last row sees, T_(b,rt) = ceil((L_b - f + i_last + 1) /
+// 32) (the same for every g); segments in order (b, g, rt) make one line of
+// TT tiles, split into P equal workgroup ranges at lo(w) = floor(w TT / P).
+// P is the fewest whole rounds
 // of the target count that keep every range within kMaxItemTiles (so all
 // workgroups of a round finish together), and at most TT. Items are the pieces of the
 // line cut at segment starts and range starts, in line order; the item that
@@ -91,7 +97,18 @@ __global__ __launch_bounds__(kPlanThreads) void k_rect_plan(RectArgs a) {
   __shared__ long long sh[kPlanThreads / 64];
   const int tid = threadIdx.x;
   const long long Hkv = c.Hkv;
-  auto tiles = [&](int b) { return (long long)(c.seq_lens[b] + kRectTileKeys - 1) / kRectTileKeys; };
+  const int RT = a.rtiles;
+  // end key (exclusive) of row tile rt of a sequence of length L
+  auto key_end = [&](int L, int rt) {
+    const int r_last = min(a.rows, (rt + 1) * a.tile_rows) - 1;
+    return max(1, L - a.f + r_last / c.G + 1);
+  };
+  auto rt_tiles = [&](int L, int rt) { return (long long)(key_end(L, rt) + kRectTileKeys - 1) / kRectTileKeys; };
+  auto tiles = [&](int b) {  // all row tiles of one (sequence, KV head)
+    long long t = 0;
+    for (int rt = 0; rt < RT; ++rt) t += rt_tiles(c.seq_lens[b], rt);
+    return t;
+  };
 
   const int per_b = (c.B + kPlanThreads - 1) / kPlanThreads;
   const int b0 = min(c.B, tid * per_b), b1 = min(c.B, b0 + per_b);
@@ -110,15 +127,17 @@ __global__ __launch_bounds__(kPlanThreads) void k_rect_plan(RectArgs a) {
   const long long q = TT / P, r = TT % P;
   __syncthreads();  // ptile visible to the workgroup
 
-  const int S = c.B * c.Hkv;
+  const int S = c.B * c.Hkv * RT;
   const int per_s = (S + kPlanThreads - 1) / kPlanThreads;
   const int s0 = min(S, tid * per_s), s1 = min(S, s0 + per_s);
   // segment s: first tile, end tile, and the range starts strictly inside
   auto segment = [&](int s, long long& as, long long& es, long long& wl, long long& wh) {
-    const int b = s / c.Hkv, g = s % c.Hkv;
-    const long long T = tiles(b);
-    as = a.ptile[b] * Hkv + g * T;
-    es = as + T;
+    const int b = s / (c.Hkv * RT), g = (s / RT) % c.Hkv, rt = s % RT;
+    const int L = c.seq_lens[b];
+    long long before = 0;  // key tiles of the sequence's earlier row tiles
+    for (int x = 0; x < rt; ++x) before += rt_tiles(L, x);
+    as = a.ptile[b] * Hkv + g * tiles(b) + before;
+    es = as + rt_tiles(L, rt);
     wl = ceil_div_ll((as + 1) * P, TT);
     wh = ceil_div_ll(es * P, TT) - 1;
   };
@@ -133,8 +152,8 @@ __global__ __launch_bounds__(kPlanThreads) void k_rect_plan(RectArgs a) {
   for (int s = s0; s < s1; ++s) {
     long long as, es, wl, wh;
     segment(s, as, es, wl, wh);
-    const int b = s / c.Hkv, g = s % c.Hkv;
-    const int L = c.seq_lens[b];
+    const int b = s / (c.Hkv * RT), g = (s / RT) % c.Hkv, rt = s % RT;
+    const int kend = key_end(c.seq_lens[b], rt);
     const int cnt = 1 + int(wh >= wl ? wh - wl + 1 : 0);
     a.groups[s] = make_int2(int(fi), cnt);
     // the range that holds tile as starts exactly there: this item is its first
@@ -144,8 +163,8 @@ __global__ __launch_bounds__(kPlanThreads) void k_rect_plan(RectArgs a) {
     long long st = as;
     for (int j = 0; j < cnt; ++j) {
       const long long en = j == cnt - 1 ? es : lo_next;
-      a.items[fi + j] = make_int4(b, g, int((st - as) * kRectTileKeys),
-                                  int(min((long long)L, (en - as) * kRectTileKeys)));
+      a.items[fi + j] = make_int4(b, g | (rt << 16), int((st - as) * kRectTileKeys),
+                                  int(min((long long)kend, (en - as) * kRectTileKeys)));
       if (j > 0) a.wg_first[wl + j - 1] = int(fi + j);
       st = en;
       lo_next += q;
@@ -206,8 +225,9 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-// grid: x = workgroup range of the plan (slots); NWV waves. Wave w owns query
-// rows 32w .. 32w + 31 (a wave past G * f rows only loads). NS tile stages.
+// grid: x = workgroup range of the plan (slots); NWV waves. In an item of row
+// tile rt, wave w owns query rows 32 (NWV rt + w) .. + 31 (a wave past the G * f
+// rows only loads). NS tile stages.
 template <int D, int NWV, int NS>
 __global__ __launch_bounds__(64 * NWV, 2) void k_rect_mfma(RectArgs a) {
   constexpr int NT = 64 * NWV;
@@ -229,7 +249,6 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_rect_mfma(RectArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
   const int G = c.G;
-  const bool has_rows = wave * 32 < a.rows;  // wave-uniform
   const int item_begin = a.wg_first[blockIdx.x], item_end = a.wg_first[blockIdx.x + 1];
 
   // Per-thread constants of the tile loads. Load li of a tile is one
@@ -273,7 +292,9 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_rect_mfma(RectArgs a) {
 
   for (int item = item_begin; item < item_end; ++item) {
     const int4 it = a.items[item];
-    const int b = it.x, g = it.y, key_lo = it.z, key_hi = it.w;
+    const int b = it.x, g = it.y & 0xffff, key_lo = it.z, key_hi = it.w;
+    const int row0 = (it.y >> 16) * 32 * NWV;       // first row of the item's row tile
+    const bool has_rows = row0 + wave * 32 < a.rows;  // wave-uniform
     const int L = c.seq_lens[b];
     const int ntiles = (key_hi - key_lo + kRectTileKeys - 1) / kRectTileKeys;
     const int first_masked = L - a.f;  // keys from here on are seen by some rows only
@@ -289,7 +310,7 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_rect_mfma(RectArgs a) {
     bf16x8_t qreg[KSTEPS];
     int limit;  // last key position the row may see (-1: padding row)
     {
-      const int r = wave * 32 + col;
+      const int r = row0 + wave * 32 + col;
       const bool live = r < a.rows;
       const int i = r / G, h = r % G;
       limit = live ? L - a.f + i : -1;
@@ -560,14 +581,16 @@ __device__ __forceinline__ float load_elem(const void* p, size_t i) {
 }
 
 // Merge the key chunks of every query row. grid: x = row group of 4, y = KV
-// head, z = sequence; 256 threads, one wave per row.
+// head, z = sequence; 256 threads, one wave per row (row R lies in row tile
+// R / tile_rows).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_rect_combine(RectArgs a, void* __restrict__ out) {
   const CacheView& c = a.c;
   const int b = blockIdx.z, g = blockIdx.y, lane = threadIdx.x & 63;
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= a.rows) return;
-  const int2 gr = a.groups[size_t(b) * c.Hkv + g];
+  const int R = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (R >= a.rows) return;
+  const int r = R % a.tile_rows;  // the row's slot in its tile's partials
+  const int2 gr = a.groups[(size_t(b) * c.Hkv + g) * a.rtiles + R / a.tile_rows];
   const int live = gr.y;
   float mx = -__builtin_inff();
   for (int sp = lane; sp < live; sp += 64) mx = fmaxf(mx, a.part_ml[((size_t(gr.x) + sp) * a.rows_pad + r) * 2]);
@@ -584,7 +607,7 @@ __global__ __launch_bounds__(256) void k_rect_combine(RectArgs a, void* __restri
 #pragma unroll
     for (int e = 0; e < D / 64; ++e) num[e] = fmaf(w, a.part_acc[slot * D + lane + 64 * e], num[e]);
   }
-  const int i = r / c.G, h = r % c.G;
+  const int i = R / c.G, h = R % c.G;
   const float inv = 1.f / den;
   const size_t o0 = ((size_t(b) * a.f + i) * c.Hq + size_t(g) * c.G + h) * D;
 #pragma unroll
@@ -661,7 +684,7 @@ hipError_t launch_mfma(const RectArgs& a, void* out, hipStream_t st) {
   hipLaunchKernelGGL(k_rect_plan, dim3(1), dim3(kPlanThreads), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = a.rows_pad <= 128 ? launch_mfma_t<D, 4, 4>(a, st) : launch_mfma_t<D, 8, 8>(a, st);
+  e = a.tile_rows == 128 ? launch_mfma_t<D, 4, 4>(a, st) : launch_mfma_t<D, 8, 8>(a, st);
   if (e != hipSuccess) return e;
   dim3 g2((a.rows + 3) / 4, c.Hkv, c.B);
   hipLaunchKernelGGL((k_rect_combine<uint16_t, D>), g2, dim3(256), 0, st, a, out);
@@ -673,21 +696,24 @@ hipError_t launch_mfma(const RectArgs& a, void* out, hipStream_t st) {
 RectPlan plan_rectify(const CacheView& c, int f) {
   RectPlan p;
   p.rows = c.G * f;
-  p.rows_pad = (p.rows + 31) / 32 * 32;
-  // one round of workgroups: two per CU with 4 waves (<= 128 rows), one with 8
-  p.target = p.rows_pad <= 128 ? 512 : 256;
+  // up to 128 rows: one tile of 4 waves; more: tiles of 256 rows (8 waves)
+  p.tile_rows = p.rows <= 128 ? 128 : 256;
+  p.rtiles = (p.rows + p.tile_rows - 1) / p.tile_rows;
+  p.rows_pad = p.rtiles == 1 ? (p.rows + 31) / 32 * 32 : p.tile_rows;
+  // one round of workgroups: two per CU with 4 waves, one with 8
+  p.target = p.tile_rows == 128 ? 512 : 256;
   // the plan adds whole rounds of workgroups while a range would exceed
   // kMaxItemTiles tiles; the launch covers the largest cache the capacities allow
-  const long long groups = (long long)c.B * c.Hkv;
-  const long long tt_max = groups * ((c.max_seq_len + kRectTileKeys - 1) / kRectTileKeys);
+  const long long segments = (long long)c.B * c.Hkv * p.rtiles;
+  const long long tt_max = segments * ((c.max_seq_len + kRectTileKeys - 1) / kRectTileKeys);
   const long long rounds = (tt_max + (long long)p.target * kMaxItemTiles - 1) / ((long long)p.target * kMaxItemTiles);
   p.slots = int(p.target * (rounds > 0 ? rounds : 1));
-  p.cap = p.slots + int(groups);  // items: one per range plus one per (sequence, KV head)
+  p.cap = p.slots + int(segments);  // items: one per range plus one per segment
   return p;
 }
 
 static size_t plan_bytes(const CacheView& c, const RectPlan& p) {
-  return align_up(size_t(p.cap) * sizeof(int4), 256) + align_up(size_t(c.B) * c.Hkv * sizeof(int2), 256) +
+  return align_up(size_t(p.cap) * sizeof(int4), 256) + align_up(size_t(c.B) * c.Hkv * p.rtiles * sizeof(int2), 256) +
          align_up(size_t(p.slots + 1) * sizeof(int), 256) + align_up(size_t(c.B) * sizeof(long long), 256);
 }
 
@@ -706,6 +732,8 @@ hipError_t launch_rectify_attention(const CacheView& c, const void* q, int f, fl
   a.f = f;
   a.rows = p.rows;
   a.rows_pad = p.rows_pad;
+  a.tile_rows = p.tile_rows;
+  a.rtiles = p.rtiles;
   a.target = p.target;
   a.slots = p.slots;
   a.scale_log2 = scale * 1.4426950408889634f;
@@ -713,7 +741,7 @@ hipError_t launch_rectify_attention(const CacheView& c, const void* q, int f, fl
   a.items = reinterpret_cast<int4*>(w);
   w += align_up(size_t(p.cap) * sizeof(int4), 256);
   a.groups = reinterpret_cast<int2*>(w);
-  w += align_up(size_t(c.B) * c.Hkv * sizeof(int2), 256);
+  w += align_up(size_t(c.B) * c.Hkv * p.rtiles * sizeof(int2), 256);
   a.wg_first = reinterpret_cast<int*>(w);
   w += align_up(size_t(p.slots + 1) * sizeof(int), 256);
   a.ptile = reinterpret_cast<long long*>(w);

@@ -180,8 +180,6 @@ resa_status resa_rectify(const resa_cache* cache, const void* q, const void* k_n
   if (!q || !k_new || !v_new || !out) return fail(RESA_ERR_INVALID, "q, k_new, v_new and out must not be NULL");
   if (f < 1 || f > resa::kMaxRectF) return fail(RESA_ERR_UNSUPPORTED, "f %d outside 1 .. %d", f, resa::kMaxRectF);
   if (f > v.max_seq_len) return fail(RESA_ERR_INVALID, "f %d exceeds max_seq_len %d", f, v.max_seq_len);
-  if (v.dtype == RESA_BF16 && v.G * f > 256)
-    return fail(RESA_ERR_UNSUPPORTED, "group size * f = %d exceeds 256 query rows", v.G * f);
   if (!(scale > 0.f) || !isfinite(scale)) return fail(RESA_ERR_INVALID, "scale must be positive and finite");
   const size_t need = resa::rectify_ws_bytes(v, f);
   if (!ws || ws_bytes < need) return fail(RESA_ERR_WORKSPACE, "rectify workspace %zu < %zu bytes", ws_bytes, need);

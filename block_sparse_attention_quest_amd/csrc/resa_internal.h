@@ -14,7 +14,7 @@ constexpr int kBlock = 16;              // tokens per page = selection block
 constexpr int kTopnThreads = 1024;      // one workgroup per (sequence, KV head)
 constexpr int kTopnMaxPerThread = 32;   // => at most 32768 blocks per sequence
 constexpr int kRectTileKeys = 32;       // keys per MFMA key tile
-constexpr int kMaxRectF = 64;
+constexpr int kMaxRectF = 1024;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -94,7 +94,9 @@ hipError_t launch_decode(const CacheView& c, const void* q, const int32_t* idx, 
 
 struct RectPlan {
   int rows;     // G * f query rows per KV head
-  int rows_pad; // rounded up to the row tile
+  int tile_rows;  // rows per row tile: 128 (4 waves) or 256 (8 waves)
+  int rtiles;   // row tiles per (sequence, KV head)
+  int rows_pad; // partial slots per item: the rows of one tile, rounded up to 32
   int target;   // workgroups aimed for (one round over the chip)
   int slots;    // workgroups launched: the most any plan within the capacities uses
   int cap;      // upper bound on work items

@@ -187,7 +187,7 @@ class ChunkedPrefill:
     Attention": rectification re-encodes recent tokens with the dense pass;
     prefill is that pass over the whole prompt). An equal-length batch of
     T-token prompts goes through resa_rectify in chunks of at most `chunk`
-    (<= 64) positions: each call writes its chunk's K/V into the pages,
+    (<= 1024) positions: each call writes its chunk's K/V into the pages,
     refreshes the touched blocks' descriptors (so the whole cache's descriptors
     are built when the last chunk lands) and returns the chunk's causal
     attention rows. Prompts of different lengths are prefilled per length.

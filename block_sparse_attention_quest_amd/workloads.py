@@ -262,8 +262,9 @@ def prompt_inputs(w: Workload) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor
 
 def prompt_32k(**kw) -> Workload:
     """Chunked prefill of one 32768-token prompt, 32q/8kv, d 128, bf16, in
-    chunks of f = 64 positions."""
-    w = Workload("gqa32x8_d128_bf16_b1_prompt32k_chunk64", "bf16", 1, 32, 8, 128, (32768,), 0, 64, 16, 0.1, 1,
+    chunks of f positions (64 unless given)."""
+    f = kw.pop("f", 64)
+    w = Workload(f"gqa32x8_d128_bf16_b1_prompt32k_chunk{f}", "bf16", 1, 32, 8, 128, (32768,), 0, f, 16, 0.1, 1,
                  (0,), True, 7)
     return w.replace(**kw) if kw else w
 

@@ -192,7 +192,7 @@ resa_status resa_sparse_decode(const resa_cache* cache, const void* q, const int
  *
  *   q            : [batch][f][num_q_heads][head_dim] (dtype)
  *   k_new, v_new : [batch][f][num_kv_heads][head_dim] (dtype)
- *   f            : 1 .. 64, and f <= seq_lens[b] for every b
+ *   f            : 1 .. 1024, and f <= seq_lens[b] for every b
  *   out          : [batch][f][num_q_heads][head_dim] (dtype)
  *   ws           : >= resa_rectify_workspace_size(cache, f) bytes
  */

@@ -57,7 +57,9 @@ def test_n_cap_and_sizes(lib):
     assert lib.resa_select_workspace_size(ctypes.byref(c)) >= 2 * 2 * 32 * 8  # scores + control block
     assert lib.resa_decode_workspace_size(ctypes.byref(c), 16) > 0
     assert lib.resa_rectify_workspace_size(ctypes.byref(c), 32) > 0
-    assert lib.resa_rectify_workspace_size(ctypes.byref(c), 65) == 0
+    assert lib.resa_rectify_workspace_size(ctypes.byref(c), 1025) == 0
+    # more rows than one row tile (G 4 x f 500): several tiles, more workspace
+    assert lib.resa_rectify_workspace_size(ctypes.byref(c), 500) > lib.resa_rectify_workspace_size(ctypes.byref(c), 32)
 
 
 @pytest.mark.parametrize("bad, status", [
@@ -137,9 +139,7 @@ def test_rectify_argument_checks(lib):
                             None) == R.RESA_ERR_INVALID
     assert lib.resa_rectify(ctypes.byref(c), buf, buf, buf, 32, ctypes.c_float(0.1), buf, buf, need - 1,
                             None) == R.RESA_ERR_WORKSPACE
-    c8 = _cache(num_q_heads=16, num_kv_heads=2)   # G = 8: 8 * 64 rows is over the limit
-    need8 = lib.resa_rectify_workspace_size(ctypes.byref(c8), 64)
-    assert lib.resa_rectify(ctypes.byref(c8), buf, buf, buf, 64, ctypes.c_float(0.1), buf, buf, need8,
+    assert lib.resa_rectify(ctypes.byref(c), buf, buf, buf, 1025, ctypes.c_float(0.1), buf, buf, 1 << 40,
                             None) == R.RESA_ERR_UNSUPPORTED
 
 

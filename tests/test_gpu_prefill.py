@@ -21,6 +21,9 @@ CASES = [
     ("bf16_g1_d64_T97_c32", "bf16", 1, 2, 2, 64, 97, 32),
     ("bf16_g8_d64_T150_c32", "bf16", 2, 16, 2, 64, 150, 32),      # 256 rows per KV head, head_dim 64
     ("bf16_g4_d128_T210_c48", "bf16", 1, 8, 2, 128, 210, 48),     # 192 rows: two waves without rows
+    ("bf16_g8_d128_T200_c64", "bf16", 1, 16, 2, 128, 200, 64),    # 512 rows: two row tiles
+    ("bf16_g4_d128_T700_c256", "bf16", 2, 8, 2, 128, 700, 256),   # 1024 rows: four row tiles
+    ("bf16_g8_d64_T300_c100", "bf16", 1, 16, 2, 64, 300, 100),    # 800 rows: a partial fourth tile
     ("bf16_g8_d128_T130_c16", "bf16", 1, 16, 2, 128, 130, 16),
     ("fp32_g4_d64_T70_c16", "fp32", 1, 4, 1, 64, 70, 16),
 ]
