@@ -288,7 +288,7 @@ def sweep(args):
     rows = []
     for L in (32768, 65536, 131072, 262144):
         steps = len(ratios) * (Wu + K) + 2
-        w = W.long_256k(prefill_lens=(L,), steps=steps, r=1.0, f=64,
+        w = W.long_256k(prefill_lens=(L,), steps=steps, r=1.0, f=max(fs),
                         planted=(int(round(0.01 * (L // 16))),))
         print(f"[sweep] context {L}: setting up", file=sys.stderr, flush=True)
         r = ResaRunner(w)
@@ -312,20 +312,14 @@ def sweep(args):
             t0 = t
             sparse[rv] = timed(lambda i: r.decode_step(t0 + i), K)
             t += K
-        # one rectification of the f newest tokens (f = 128 as two calls of 64)
+        # one rectification of the f newest tokens
         rect = {}
         for f in fs:
             g = torch.Generator().manual_seed(f)
-            n64 = (f + 63) // 64
-            ins = [tuple(torch.randn(1, min(64, f), hh, 128, generator=g).to(torch.bfloat16).cuda()
-                         for hh in (32, 8, 8)) for _ in range(n64)]
+            ins = tuple(torch.randn(1, f, hh, 128, generator=g).to(torch.bfloat16).cuda() for hh in (32, 8, 8))
 
-            def event(_i, ins=ins, f=f, n64=n64):
-                for c in range(n64):
-                    fc = min(64, f - 64 * c)
-                    # the c-th call ends (n64 - 1 - c) * 64 tokens before the newest
-                    row = t - (n64 - 1 - c) * 64
-                    r.rectify(row - 1, *ins[c], f=fc)
+            def event(_i, ins=ins, f=f):
+                r.rectify(t - 1, *ins, f=f)
             event(0)
             rect[f] = timed(event, max(4, K // 8))
         row = {"context": L, "dense_decode_us": round(dense, 1),
