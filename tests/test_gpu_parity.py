@@ -114,6 +114,33 @@ def test_small_schedules_unfused_append(case):
     _run_loop_parity(w, fused_append=False)
 
 
+def test_append_select_with_the_token_already_in_the_cache():
+    """resa_append_select with k_new = v_new = NULL: the caller has written the
+    step's token itself; only its block's descriptor is refreshed before the
+    selection (the same result as passing the token)."""
+    from block_sparse_attention_quest_amd import resa as R
+    w = W.Workload("append_null", "bf16", 3, 8, 2, 128, (31, 300, 1000), 6, 0, 4, 0.1, 1, (0, 1, 2), True, 19)
+    a, b = _runner(w), _runner(w)
+    for t in range(w.steps):
+        a.decode_step(t)
+        b.set_step_lens(t + 1)
+        q, k, v = (b.step_inputs[x][t] for x in ("q", "k", "v"))
+        for s in range(w.batch):  # write the token where the append would
+            pos = w.prefill_lens[s] + t
+            page = int(b.block_table_cpu[s, pos // 16])
+            b.cache.k_pages[page, :, pos % 16] = k[s, 0]
+            b.cache.v_pages[page, :, :, pos % 16] = v[s, 0]
+        R.resa_append_select(b.cache, None, None, q, b.params, b.idx, b.count, b.n_cap, b.ws)
+        R.resa_sparse_decode(b.cache, q, b.idx, b.count, b.n_cap, b.out, b.ws, b.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(a.count, b.count), t
+        for s in range(w.batch):
+            n = int(a.count[s])
+            assert torch.equal(a.idx[s, :, :n], b.idx[s, :, :n]), (t, s)
+        assert torch.equal(a.out, b.out), t
+    assert torch.equal(a.cache.desc, b.cache.desc)
+
+
 def test_fused_and_unfused_append_agree():
     """resa_append_select leaves the cache, descriptors, selection and output
     exactly as resa_update_descriptors + resa_select_blocks do."""
@@ -167,9 +194,12 @@ def _rect_inputs(w, f, seed):
     return q, k, v
 
 
-def test_rectify_mixed_lengths_small():
-    """Mixed-length batch, f = 64, G * f = 256 query rows per KV head (two row tiles per wave)."""
-    w = W.rectify_mixed(batch=4, len_range=(100, 3000), seed=21)
+@pytest.mark.parametrize("f", [64, 100], ids=["f64_one_row_tile", "f100_two_row_tiles"])
+def test_rectify_mixed_lengths_small(f):
+    """Mixed-length batch, G * f = 256 query rows per KV head (one row tile of
+    8 waves) or 400 (a full tile of 256 rows and a partial one of 144)."""
+    w = W.rectify_mixed(batch=4, len_range=(150, 3000), seed=21, f=f)
+    print(f"[case] mixed rectify f={f} lens={w.prefill_lens}", flush=True)
     r = _runner(w)
     oc = P.oracle_cache(w)
     got = r.rectify_only()
