@@ -526,6 +526,21 @@ def main():
                "decode": 1e3 * sum(e[2].elapsed_time(e[3]) for e in cold_ev) / COLD_REPS - pair_us}
     del flush, sink
 
+    # ---- a plain device copy of 1 GiB (read + write), the box's own
+    # streaming reference beside the published peak ----
+    src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    times_copy = []
+    for _ in range(5):
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        dst.copy_(src)
+        c1.record(stream)
+        c1.synchronize()
+        times_copy.append(c0.elapsed_time(c1))
+    copy_gbs = 2 * src.numel() / (sorted(times_copy)[2] * 1e-3) / 1e9
+    del src, dst
+
     # ---- algorithmic work at the middle of the timed region ----
     tm = Wu + K // 2
     L_list = [L + tm + 1 for L in w.prefill_lens]
@@ -572,6 +587,8 @@ def main():
         "cold_cache_us": {k: round(v, 2) for k, v in cold_us.items()},
         "cold_decode_gbs": round(sb["decode"] / (cold_us["decode"] * 1e-6) / 1e9, 1),
         "append_select_gbs": round(sel_gbs, 1),
+        "copy_1gib_gbs": round(copy_gbs, 1),
+        "decode_frac_of_copy": round(dec_gbs / copy_gbs, 3),
         "decode_gbs": round(dec_gbs, 1),
         "sparse_steps_per_s": round(1e6 / (stage_us["append_select"] + stage_us["decode"]), 1),
         "rectify": {"us": rect_us and round(rect_us, 1), "tflops": rect_tflops and round(rect_tflops, 1),
