@@ -180,14 +180,6 @@ __global__ __launch_bounds__(kPlanThreads) void k_rect_plan(RectArgs a) {
 }
 
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(1))) const void* global_ptr_t;
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-// Wait until at most N vector-memory instructions of this wave are in flight.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  __builtin_amdgcn_s_waitcnt(((N >> 4) & 3) << 14 | (0xF << 8) | (7 << 4) | (N & 15));
-}
 
 // Wait until this wave's LDS accesses are done.
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt((3 << 14) | (7 << 4) | 15); }

@@ -12,18 +12,24 @@
 // bf16/fp32 keys are exact. A block's descriptor record for one head is
 // 2 x head_dim contiguous elements; head_dim/8 lanes read it with 16-byte loads
 // (all of a lane's loads are issued before any is used), and the lanes' float64
-// partials are summed with DPP moves inside a row. Scores go to the workspace.
+// partials are summed with DPP moves inside a row. Each score goes to the
+// workspace as its order-preserving 64-bit key (unsigned order of keys is the
+// numeric order of scores, -0 and +0 equal), in rows of an even stride.
 //
 // k_topn, grid (KV head, sequence), 1024 threads: n = min(M, max(n_min,
 // ceil(M r))) in IEEE double; the min(n_local, n) newest blocks are always
 // taken; the other places go to the highest scores, ties to the lower index.
-// The candidates' order-preserving 64-bit keys stay in registers (each thread
-// issues exactly as many score loads as the longest sequence needs). The
-// threshold is found exactly by radix selection with 12-bit digits starting
-// below the common prefix of the candidates' key range (usually one pass)
-// until the candidates that share the threshold's prefix number at most 64;
-// one wave then ranks those exactly (key descending, index ascending). Chosen blocks are marked in an LDS
-// bitmap and compacted in index order, so the output is sorted ascending.
+// The candidates' keys stay in registers (each thread issues exactly as many
+// loads as the longest sequence needs, before the sequence length arrives).
+// The threshold is found exactly by radix selection with 12-bit digits
+// starting below the common prefix of the candidates' key range (usually one
+// pass) until the candidates that share the threshold's prefix number at most
+// 64. Chosen blocks are marked in an LDS bitmap from ballots; the members of
+// that last group are listed per wave and ranked exactly (key descending,
+// index ascending) by one wave, a member per lane. The bitmap
+// is compacted in index order, so the output is sorted ascending. Prefix sums
+// and reductions run on DPP lane moves; values every lane shares are moved to
+// scalar registers so that the per-mode branches are scalar.
 //
 // The two kernels hand over through the workspace at the kernel boundary: a
 // cross-workgroup hand-off inside one kernel would need device-scope fences,
@@ -72,6 +78,14 @@ __device__ __forceinline__ int select_count(int M, const resa_select_params& p) 
   return min(M, max(p.n_min, int(ceil(double(M) * p.r))));
 }
 
+// Order-preserving key of a score: unsigned comparison of keys is numeric
+// comparison of scores, with -0 and +0 equal.
+__device__ __forceinline__ uint64_t order_key(double s) {
+  if (s == 0.0) s = 0.0;
+  const uint64_t u = uint64_t(__double_as_longlong(s));
+  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double x) {
   const uint64_t u = uint64_t(__double_as_longlong(x));
@@ -99,7 +113,7 @@ __device__ __forceinline__ double row_sum_f64(double x) {
 // workgroup reads because with n_local >= 1 it is always forced.
 template <typename T, int D>
 __global__ __launch_bounds__(kScoreThreads) void k_score(CacheView c, const void* __restrict__ q,
-                                                         resa_select_params p, double* __restrict__ scores,
+                                                         resa_select_params p, uint64_t* __restrict__ keys,
                                                          bool append, const void* __restrict__ k_new,
                                                          const void* __restrict__ v_new) {
   constexpr int LPB = D / 8;     // lanes per block record (8 channels each)
@@ -159,118 +173,121 @@ __global__ __launch_bounds__(kScoreThreads) void k_score(CacheView c, const void
       for (int e = 0; e < 8; ++e) part += qb[e] * double(qb[e] >= 0.0 ? hi[r].get(e) : lo[r].get(e));
     }
     part = row_sum_f64<LPB>(part);
-    if (sub == 0 && jr[r] < Mo) scores[gi * c.maxb + jr[r]] = part;
+    if (sub == 0 && jr[r] < Mo) keys[gi * key_stride(c.maxb) + jr[r]] = order_key(part);
   }
 }
 
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t x) {
-  const int lo = __builtin_amdgcn_mov_dpp(int(uint32_t(x)), CTRL, 0xF, 0xF, false);
-  const int hi = __builtin_amdgcn_mov_dpp(int(uint32_t(x >> 32)), CTRL, 0xF, 0xF, false);
-  return (uint64_t(uint32_t(hi)) << 32) | uint32_t(lo);
-}
-
-// Maximum (MAX) or minimum over each row of 16 lanes, every lane of the row
-// gets it (four DPP steps).
+// Maximum (MAX) or minimum of x over each row of 16 lanes; every lane of the
+// row gets it (four DPP steps).
 template <bool MAX>
-__device__ __forceinline__ uint64_t row_reduce_u64(uint64_t x) {
-  auto pick = [](uint64_t a, uint64_t b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
-  x = pick(x, dpp_u64<kDppQuadXor1>(x));
-  x = pick(x, dpp_u64<kDppQuadXor2>(x));
-  x = pick(x, dpp_u64<kDppHalfMirror>(x));
-  return pick(x, dpp_u64<kDppRowMirror>(x));
+__device__ __forceinline__ uint32_t row_reduce_u32(uint32_t x) {
+  auto pick = [](uint32_t a, uint32_t b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
+  x = pick(x, uint32_t(__builtin_amdgcn_mov_dpp(int(x), kDppQuadXor1, 0xF, 0xF, false)));
+  x = pick(x, uint32_t(__builtin_amdgcn_mov_dpp(int(x), kDppQuadXor2, 0xF, 0xF, false)));
+  x = pick(x, uint32_t(__builtin_amdgcn_mov_dpp(int(x), kDppHalfMirror, 0xF, 0xF, false)));
+  return pick(x, uint32_t(__builtin_amdgcn_mov_dpp(int(x), kDppRowMirror, 0xF, 0xF, false)));
 }
 
-// The same over the 64 lanes of a wave: the rows, then two lane swaps across
-// rows.
+// The same over the 64 lanes of a wave: the rows, then their four results
+// read out into scalars.
 template <bool MAX>
-__device__ __forceinline__ uint64_t wave_reduce_u64(uint64_t x) {
-  auto pick = [](uint64_t a, uint64_t b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
-  x = row_reduce_u64<MAX>(x);
-  x = pick(x, uint64_t(__shfl_xor((unsigned long long)x, 16, 64)));
-  x = pick(x, uint64_t(__shfl_xor((unsigned long long)x, 32, 64)));
-  return x;
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t x) {
+  auto pick = [](uint32_t a, uint32_t b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
+  x = row_reduce_u32<MAX>(x);
+  const uint32_t a = __builtin_amdgcn_readlane(x, 0), b = __builtin_amdgcn_readlane(x, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(x, 32), d = __builtin_amdgcn_readlane(x, 48);
+  return pick(pick(a, b), pick(c, d));
 }
 
-__device__ __forceinline__ uint64_t order_key(double s) {
-  if (s == 0.0) s = 0.0;  // -0 and +0 are equal scores
-  const uint64_t u = uint64_t(__double_as_longlong(s));
-  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+// Inclusive prefix sum inside each row of 16 lanes (DPP row shifts by 1, 2, 4
+// and 8; a lane with no source lane adds 0).
+__device__ __forceinline__ int row_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr1, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr1 + 1, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr1 + 3, 0xF, 0xF, false);
+  return x + __builtin_amdgcn_update_dpp(0, x, kDppRowShr1 + 7, 0xF, 0xF, false);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: the rows, then the last
+// lane of row 0 added into rows 1 and 3 (of row 2 into row 3), then that of
+// row 1 into rows 2 and 3.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x = row_incl_scan(x);
+  x += __builtin_amdgcn_update_dpp(0, x, kDppRowBcast15, 0xA, 0xF, false);
+  return x + __builtin_amdgcn_update_dpp(0, x, kDppRowBcast31, 0xC, 0xF, false);
+}
+
+// A value every lane of the wave holds, moved to a scalar register so that
+// branches on it are scalar branches.
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ uint32_t uniform(uint32_t x) { return uint32_t(__builtin_amdgcn_readfirstlane(int(x))); }
+
+// Exclusive prefix sum of v over the 1024 threads; `total` gets the sum. One
+// barrier. `tmp` (one int per wave) must not be in use by another scan that
+// some wave may still be reading.
+__device__ __forceinline__ int wg_exclusive_scan(int v, int* tmp, int& total) {
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(int(threadIdx.x >> 6));
+  const int x = wave_incl_scan(v);
+  if (lane == 63) tmp[wave] = x;
+  __syncthreads();
+  const int w = row_incl_scan(lane < kTopnWaves ? tmp[lane] : 0);  // lanes 0 .. 15: waves 0 .. lane
+  total = __builtin_amdgcn_readlane(w, kTopnWaves - 1);
+  const int before = wave == 0 ? 0 : __builtin_amdgcn_readlane(w, wave - 1);
+  return before + x - v;
 }
 
 constexpr int kTopnBits = 12;
 constexpr int kTopnBins = 1 << kTopnBits;  // 4 bins per thread
 
-struct TopnSmem {
-  int hist[kTopnBins];
+// Selection state in LDS. The histogram is dead once the threshold is known,
+// so the bitmaps and the ranked group's lists reuse its space.
+struct TopnAfter {
   uint32_t sel[kBitmapWords];
   uint32_t tie[kBitmapWords];
-  uint64_t red_max[kTopnWaves], red_min[kTopnWaves];
-  int scan[kTopnWaves];
-  uint64_t gk[kRankGroup];
-  int gj[kRankGroup];
-  int gcount;
+  uint64_t gk[kTopnWaves][kRankGroup];  // ranked group: each wave's members in its own order
+  int gj[kTopnWaves][kRankGroup];
+};
+struct alignas(16) TopnShared {
+  union {
+    int hist[kTopnBins];
+    TopnAfter a;
+  } u;
+  uint32_t red[4][kTopnWaves];  // per wave: max, min of the keys' high words, then of the low words
+  int scan_a[kTopnWaves], scan_b[kTopnWaves];
+  int gcount[kTopnWaves];
   int digit, k_rem, gsize;
 };
-
-// Exclusive scan over the 1024 threads; `total` gets the sum.
-__device__ __forceinline__ int wg_exclusive_scan(int v, int* tmp, int& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) tmp[wave] = x;
-  __syncthreads();
-  int before = 0;
-  total = 0;
-#pragma unroll
-  for (int w = 0; w < kTopnWaves; ++w) {
-    const int t = tmp[w];
-    before += w < wave ? t : 0;
-    total += t;
-  }
-  __syncthreads();
-  return before + x - v;
-}
-
-// grid: x = KV head, y = sequence; 1024 threads. EMAX >= ceil(M / 1024) keys
-// per thread, so every thread issues exactly EMAX score loads.
+// Keys in registers: EMAX per thread, block j = e * 1024 + tid, all loads
+// issued together (slots past the row re-read entry 0 and are ignored). The
+// per-block steps are unrolled over the EMAX registers.
 template <int EMAX>
-__global__ __launch_bounds__(kTopnThreads) void k_topn(const double* __restrict__ scores,
-                                                       const int32_t* __restrict__ seq_lens, int maxb,
-                                                       int Hkv, resa_select_params p, int32_t* __restrict__ idx,
-                                                       int32_t* __restrict__ count, int n_cap) {
-  __shared__ TopnSmem sm;
-  const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int L = seq_lens[b];
-  const int M = (L + kBlock - 1) / kBlock;
-  const int n = select_count(M, p);
-  if (g == 0 && tid == 0) count[b] = n;
-  const int keep = min(p.n_local, n);
-  const int quota = n - keep;
-  const int Mo = M - keep;  // candidates: blocks 0 .. Mo-1
-  const size_t gi = size_t(b) * Hkv + g;
-  const double* row = scores + gi * maxb;
-
-  // keys of the candidates, block j = e * 1024 + tid (loads issued together;
-  // out-of-range slots re-read block 0 and are ignored)
-  uint64_t key[EMAX];
-  {
-    double sc[EMAX];
+struct RegKeys {
+  uint64_t k[EMAX];
+  __device__ void load(const uint64_t* row, int len) {
 #pragma unroll
     for (int e = 0; e < EMAX; ++e) {
-      const int j = e * kTopnThreads + tid;
-      sc[e] = row[j < Mo ? j : 0];
+      const int j = e * kTopnThreads + int(threadIdx.x);
+      k[e] = row[j < len ? j : 0];
     }
-#pragma unroll
-    for (int e = 0; e < EMAX; ++e) key[e] = order_key(sc[e]);
   }
-  for (int i = tid; i < kTopnBins; i += kTopnThreads) sm.hist[i] = 0;
-  if (tid == 0) sm.gcount = 0;
+  template <class F>
+  __device__ __forceinline__ void each(F&& f) const {
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) f(e * kTopnThreads + int(threadIdx.x), k[e]);
+  }
+};
+
+// Selection of one (sequence, KV head) row. keys.each(f) calls f(j, key) for
+// every block j < M (and past it, up to the register count), with the same
+// j - lane across a wave; out is the row of idx.
+template <class Keys>
+__device__ __forceinline__ void topn_row(const Keys& keys, TopnShared& sm, int M, int n, int keep,
+                                         int32_t* __restrict__ out) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uniform(int(tid >> 6));
+  const int quota = n - keep;
+  const int Mo = M - keep;  // candidates: blocks 0 .. Mo-1
 
   // mode: 0 none of the candidates, 1 every member of the prefix group,
   // 2 the lowest indices of the (exactly tied) prefix group, 3 ranked group
@@ -278,31 +295,56 @@ __global__ __launch_bounds__(kTopnThreads) void k_topn(const double* __restrict_
   uint64_t prefix = 0, mask = 0;
   int k = quota;
   if (quota > 0) {
-    uint64_t kmax = 0, kmin = ~0ull;
-#pragma unroll
-    for (int e = 0; e < EMAX; ++e) {
-      if (e * kTopnThreads + tid < Mo) {
-        kmax = key[e] > kmax ? key[e] : kmax;
-        kmin = key[e] < kmin ? key[e] : kmin;
+    reinterpret_cast<int4*>(sm.u.hist)[tid] = int4{0, 0, 0, 0};  // kTopnBins = 4 x 1024
+    // the candidates' key range, high words first; the low words only when
+    // every high word is the same
+    uint32_t hmax = 0, hmin = ~0u;
+    keys.each([&](int j, uint64_t key) {
+      if (j < Mo) {
+        const uint32_t h = uint32_t(key >> 32);
+        hmax = h > hmax ? h : hmax;
+        hmin = h < hmin ? h : hmin;
       }
-    }
-    kmax = wave_reduce_u64<true>(kmax);
-    kmin = wave_reduce_u64<false>(kmin);
+    });
+    hmax = wave_reduce_u32<true>(hmax);
+    hmin = wave_reduce_u32<false>(hmin);
     if (lane == 0) {
-      sm.red_max[wave] = kmax;
-      sm.red_min[wave] = kmin;
+      sm.red[0][wave] = hmax;
+      sm.red[1][wave] = hmin;
     }
     __syncthreads();
-    // lanes 0 .. 15 of every wave take one wave's result each, then reduce them
+    // lanes 0 .. 15 of every row take one wave's result each, then reduce them
     // inside the row of 16
-    kmax = sm.red_max[lane & (kTopnWaves - 1)];
-    kmin = sm.red_min[lane & (kTopnWaves - 1)];
-    kmax = row_reduce_u64<true>(kmax);
-    kmin = row_reduce_u64<false>(kmin);
-    const int plen = kmax == kmin ? 64 : __clzll((long long)(kmax ^ kmin));
+    hmax = uniform(row_reduce_u32<true>(sm.red[0][lane & (kTopnWaves - 1)]));
+    hmin = uniform(row_reduce_u32<false>(sm.red[1][lane & (kTopnWaves - 1)]));
+    int plen;
+    if (hmax != hmin) {
+      plen = __clz(hmax ^ hmin);
+      prefix = uint64_t(hmax) << 32;
+    } else {
+      uint32_t lmax = 0, lmin = ~0u;
+      keys.each([&](int j, uint64_t key) {
+        if (j < Mo) {
+          const uint32_t l = uint32_t(key);
+          lmax = l > lmax ? l : lmax;
+          lmin = l < lmin ? l : lmin;
+        }
+      });
+      lmax = wave_reduce_u32<true>(lmax);
+      lmin = wave_reduce_u32<false>(lmin);
+      if (lane == 0) {
+        sm.red[2][wave] = lmax;
+        sm.red[3][wave] = lmin;
+      }
+      __syncthreads();
+      lmax = uniform(row_reduce_u32<true>(sm.red[2][lane & (kTopnWaves - 1)]));
+      lmin = uniform(row_reduce_u32<false>(sm.red[3][lane & (kTopnWaves - 1)]));
+      plen = 32 + (lmax == lmin ? 32 : __clz(lmax ^ lmin));
+      prefix = (uint64_t(hmax) << 32) | lmax;
+    }
     mask = plen == 0 ? 0ull : (~0ull << (64 - plen));
-    prefix = kmax & mask;
-    int gsize = Mo;  // every candidate lies in [kmin, kmax], so shares the prefix
+    prefix &= mask;
+    int gsize = Mo;  // every candidate lies in the range, so shares its prefix
     int bits_left = 64 - plen;
     bool first = true;
     while (gsize > kRankGroup && gsize != k && bits_left > 0) {
@@ -311,27 +353,26 @@ __global__ __launch_bounds__(kTopnThreads) void k_topn(const double* __restrict_
       const int nbins = 1 << nb;
       const bool first_pass = first;
       if (!first) {
-        for (int i = tid; i < kTopnBins; i += kTopnThreads) sm.hist[i] = 0;
+        reinterpret_cast<int4*>(sm.u.hist)[tid] = int4{0, 0, 0, 0};
         __syncthreads();
       }
       first = false;
-#pragma unroll
-      for (int e = 0; e < EMAX; ++e) {
-        // the first pass takes every candidate: all share the range's prefix
-        if (e * kTopnThreads + tid < Mo && (first_pass || (key[e] & mask) == prefix))
-          atomicAdd(&sm.hist[int(key[e] >> shift) & (nbins - 1)], 1);
-      }
+      // the first pass takes every candidate: all share the range's prefix
+      keys.each([&](int j, uint64_t key) {
+        if (j < Mo && (first_pass || (key & mask) == prefix))
+          atomicAdd(&sm.u.hist[int(key >> shift) & (nbins - 1)], 1);
+      });
       __syncthreads();
       // thread t owns the 4 digits nbins-1-4t .. nbins-4-4t (from the top)
       int h[4], mine = 0;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int d = nbins - 1 - (4 * tid + u);
-        h[u] = d >= 0 ? sm.hist[d] : 0;
+        h[u] = d >= 0 ? sm.u.hist[d] : 0;
         mine += h[u];
       }
       int total;
-      int above = wg_exclusive_scan(mine, sm.scan, total);
+      int above = wg_exclusive_scan(mine, sm.scan_a, total);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         if (above < k && above + h[u] >= k) {
@@ -342,72 +383,92 @@ __global__ __launch_bounds__(kTopnThreads) void k_topn(const double* __restrict_
         above += h[u];
       }
       __syncthreads();
-      prefix |= uint64_t(sm.digit) << shift;
+      prefix |= uint64_t(uniform(sm.digit)) << shift;
       mask |= uint64_t(nbins - 1) << shift;
-      k = sm.k_rem;
-      gsize = sm.gsize;
+      k = uniform(sm.k_rem);
+      gsize = uniform(sm.gsize);
       bits_left -= nb;
     }
     mode = gsize == k ? 1 : (bits_left == 0 ? 2 : 3);
   }
   // mark the chosen blocks: a wave's 64 consecutive blocks are two bitmap
   // words, stored whole by its first lane from ballots (each word has exactly
-  // one writer, so no clearing or atomics are needed); in mode 3 the members
-  // of the threshold's prefix group are gathered for ranking on the way
-#pragma unroll
-  for (int e = 0; e < EMAX; ++e) {
-    const int j = e * kTopnThreads + tid;
-    bool s = false, t = false;
-    if (j < Mo) {
-      const uint64_t km = key[e] & mask;
-      const bool above = km > prefix, at = km == prefix;
-      s = mode != 0 && (above || (at && mode == 1));
-      t = at && mode == 2;
-      if (at && mode == 3) {
-        const int slot = atomicAdd(&sm.gcount, 1);
-        sm.gk[slot] = key[e];
-        sm.gj[slot] = j;
-      }
-    } else if (j < M) {
-      s = true;
-    }
+  // one writer, so no clearing or atomics are needed); in mode 3 every wave
+  // lists its members of the threshold's prefix group (at most 64 in all)
+  int wcount = 0;  // wave-uniform
+  // (key & mask) > prefix  <=>  key > prefix | ~mask;  (key & mask) >= prefix  <=>  key >= prefix
+  const uint64_t top = prefix | ~mask;
+  const bool any = mode != 0, take_eq = mode == 1;
+  keys.each([&](int j, uint64_t key) {
+    const bool cand = j < Mo;
+    const bool gt = key > top, ge = key >= prefix;
+    const bool s = (cand & any & (gt | (ge & take_eq))) | (!cand & (j < M));
+    const bool at = cand & ge & !gt;
     const uint64_t bs = __builtin_amdgcn_ballot_w64(s);
-    const int w0 = (e * kTopnThreads + wave * 64) >> 5;
+    const int w0 = (j - lane) >> 5;
     if (lane == 0) {
-      sm.sel[w0] = uint32_t(bs);
-      sm.sel[w0 + 1] = uint32_t(bs >> 32);
+      sm.u.a.sel[w0] = uint32_t(bs);
+      sm.u.a.sel[w0 + 1] = uint32_t(bs >> 32);
     }
-    if (mode == 2) {  // the tie words are read in mode 2 only
-      const uint64_t bt = __builtin_amdgcn_ballot_w64(t);
-      if (lane == 0) {
-        sm.tie[w0] = uint32_t(bt);
-        sm.tie[w0 + 1] = uint32_t(bt >> 32);
+    if (mode >= 2) {
+      const uint64_t bt = __builtin_amdgcn_ballot_w64(at);
+      if (mode == 2) {  // the tie words are read in mode 2 only
+        if (lane == 0) {
+          sm.u.a.tie[w0] = uint32_t(bt);
+          sm.u.a.tie[w0 + 1] = uint32_t(bt >> 32);
+        }
+      } else if (bt) {
+        if (at) {
+          const int slot = wcount + int(__builtin_amdgcn_mbcnt_hi(uint32_t(bt >> 32),
+                                                                  __builtin_amdgcn_mbcnt_lo(uint32_t(bt), 0u)));
+          sm.u.a.gk[wave][slot] = key;
+          sm.u.a.gj[wave][slot] = j;
+        }
+        wcount += __builtin_popcountll(bt);
       }
     }
-  }
+  });
+  if (mode == 3 && lane == 0) sm.gcount[wave] = wcount;
   __syncthreads();
-  if (mode == 3 && tid < 64) {  // wave 0 ranks the gathered group, one candidate per lane
-    const int gs = sm.gcount;
-    const uint64_t kt = tid < gs ? sm.gk[tid] : 0;
-    const int jt = tid < gs ? sm.gj[tid] : 0;
+  if (mode == 3 && wave == 0) {
+    // ranked group (key descending, index ascending; usually a handful of
+    // blocks): member i in lane i (the waves' lists laid end to end), then
+    // every member counts the members that come before it
+    const int incl = row_incl_scan(lane < kTopnWaves ? sm.gcount[lane] : 0);
+    const int gs = __builtin_amdgcn_readlane(incl, kTopnWaves - 1);
+    int owner = 0, base = 0;
+#pragma unroll
+    for (int w = 0; w < kTopnWaves - 1; ++w) {
+      const int iw = __builtin_amdgcn_readlane(incl, w);
+      if (iw <= lane) {
+        owner = w + 1;
+        base = iw;
+      }
+    }
+    uint64_t kt = 0;
+    int jt = 0;
+    if (lane < gs) {
+      kt = sm.u.a.gk[owner][lane - base];
+      jt = sm.u.a.gj[owner][lane - base];
+    }
     const uint32_t klo = uint32_t(kt), khi = uint32_t(kt >> 32);
     int rank = 0;
-    for (int u = 0; u < gs; ++u) {  // candidate u broadcast from its lane
+    for (int u = 0; u < gs; ++u) {
       const uint64_t ku = (uint64_t(uint32_t(__builtin_amdgcn_readlane(khi, u))) << 32) |
                           uint32_t(__builtin_amdgcn_readlane(klo, u));
       const int ju = __builtin_amdgcn_readlane(jt, u);
       rank += (ku > kt || (ku == kt && ju < jt)) ? 1 : 0;
     }
-    if (tid < gs && rank < k) atomicOr(&sm.sel[jt >> 5], 1u << (jt & 31));
+    if (lane < gs && rank < k) atomicOr(&sm.u.a.sel[jt >> 5], 1u << (jt & 31));
   }
-  __syncthreads();
+  if (mode == 3) __syncthreads();
   // exactly tied threshold group: the k lowest indices
   const int W = (M + 31) / 32;
-  uint32_t word = tid < W ? sm.sel[tid] : 0u;
+  uint32_t word = tid < W ? sm.u.a.sel[tid] : 0u;
   if (mode == 2) {
-    const uint32_t tw = tid < W ? sm.tie[tid] : 0u;
+    const uint32_t tw = tid < W ? sm.u.a.tie[tid] : 0u;
     int total;
-    int before = wg_exclusive_scan(__builtin_popcount(tw), sm.scan, total);
+    int before = wg_exclusive_scan(__builtin_popcount(tw), sm.scan_a, total);
     uint32_t f = tw;
     while (f) {
       const uint32_t bit = f & (~f + 1u);
@@ -416,8 +477,7 @@ __global__ __launch_bounds__(kTopnThreads) void k_topn(const double* __restrict_
     }
   }
   int total;
-  int pos = wg_exclusive_scan(__builtin_popcount(word), sm.scan, total);
-  int32_t* out = idx + gi * n_cap;
+  int pos = wg_exclusive_scan(__builtin_popcount(word), sm.scan_b, total);
   while (word && pos < n) {  // exactly n bits are set; the bound keeps every store in the row
     const int e = __builtin_ctz(word);
     word &= word - 1u;
@@ -425,12 +485,32 @@ __global__ __launch_bounds__(kTopnThreads) void k_topn(const double* __restrict_
   }
 }
 
+// grid: x = KV head, y = sequence; 1024 threads. EMAX >= ceil(M / 1024) keys
+// per thread, held in registers.
+template <int EMAX>
+__global__ __launch_bounds__(kTopnThreads) void k_topn(const uint64_t* __restrict__ keys, int stride,
+                                                       const int32_t* __restrict__ seq_lens, int Hkv,
+                                                       resa_select_params p, int32_t* __restrict__ idx,
+                                                       int32_t* __restrict__ count, int n_cap) {
+  __shared__ TopnShared sm;
+  const int g = blockIdx.x, b = blockIdx.y;
+  const size_t gi = size_t(b) * Hkv + g;
+  RegKeys<EMAX> rk;
+  rk.load(keys + gi * stride, stride);  // issued before the sequence length arrives
+  const int L = seq_lens[b];
+  const int M = (L + kBlock - 1) / kBlock;
+  const int n = select_count(M, p);
+  if (g == 0 && threadIdx.x == 0) count[b] = n;
+  topn_row(rk, sm, M, n, min(p.n_local, n), idx + gi * n_cap);
+}
+
 hipError_t launch_topn(const CacheView& c, const resa_select_params& p, int32_t* idx, int32_t* count,
-                       int n_cap, const double* scores, hipStream_t s) {
+                       int n_cap, const uint64_t* keys, hipStream_t s) {
   const int mmax = (c.max_seq_len + kBlock - 1) / kBlock;
-  const int e = (mmax + kTopnThreads - 1) / kTopnThreads;
+  const int stride = key_stride(c.maxb);
   dim3 grid(c.Hkv, c.B);
-#define RESA_TOPN(E) hipLaunchKernelGGL(k_topn<E>, grid, dim3(kTopnThreads), 0, s, scores, c.seq_lens, c.maxb, \
+  const int e = (mmax + kTopnThreads - 1) / kTopnThreads;
+#define RESA_TOPN(E) hipLaunchKernelGGL(k_topn<E>, grid, dim3(kTopnThreads), 0, s, keys, stride, c.seq_lens, \
                                         c.Hkv, p, idx, count, n_cap)
   // every thread handles EMAX keys: exact up to 18 (256K context), then
   // coarser steps
@@ -456,29 +536,31 @@ hipError_t launch_topn(const CacheView& c, const resa_select_params& p, int32_t*
 
 template <typename T, int D>
 hipError_t launch_select_t(const CacheView& c, const void* q, const resa_select_params& p, int32_t* idx,
-                           int32_t* count, int n_cap, double* scores, bool append, const void* k_new,
+                           int32_t* count, int n_cap, uint64_t* keys, bool append, const void* k_new,
                            const void* v_new, hipStream_t s) {
   dim3 g1((c.maxb + kScoreChunk - 1) / kScoreChunk + (append ? 1 : 0), c.Hkv, c.B);
-  hipLaunchKernelGGL((k_score<T, D>), g1, dim3(kScoreThreads), 0, s, c, q, p, scores, append, k_new, v_new);
+  hipLaunchKernelGGL((k_score<T, D>), g1, dim3(kScoreThreads), 0, s, c, q, p, keys, append, k_new, v_new);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_topn(c, p, idx, count, n_cap, scores, s);
+  return launch_topn(c, p, idx, count, n_cap, keys, s);
 }
 
 }  // namespace
 
-size_t select_ws_bytes(const CacheView& c) { return size_t(c.B) * c.Hkv * c.maxb * sizeof(double); }
+// The keys' rows, 16-byte aligned (one extra piece of slack for aligning the
+// caller's pointer).
+size_t select_ws_bytes(const CacheView& c) { return size_t(c.B) * c.Hkv * key_stride(c.maxb) * sizeof(uint64_t) + 16; }
 
 namespace {
 hipError_t select_dispatch(const CacheView& c, const void* q, const resa_select_params& p, int32_t* idx,
                            int32_t* count, int n_cap, void* ws, bool append, const void* k_new,
                            const void* v_new, hipStream_t s) {
-  double* scores = static_cast<double*>(ws);
+  uint64_t* keys = reinterpret_cast<uint64_t*>((reinterpret_cast<uintptr_t>(ws) + 15) & ~uintptr_t(15));
   if (c.dtype == RESA_BF16)
-    return c.D == 128 ? launch_select_t<uint16_t, 128>(c, q, p, idx, count, n_cap, scores, append, k_new, v_new, s)
-                      : launch_select_t<uint16_t, 64>(c, q, p, idx, count, n_cap, scores, append, k_new, v_new, s);
-  return c.D == 128 ? launch_select_t<float, 128>(c, q, p, idx, count, n_cap, scores, append, k_new, v_new, s)
-                    : launch_select_t<float, 64>(c, q, p, idx, count, n_cap, scores, append, k_new, v_new, s);
+    return c.D == 128 ? launch_select_t<uint16_t, 128>(c, q, p, idx, count, n_cap, keys, append, k_new, v_new, s)
+                      : launch_select_t<uint16_t, 64>(c, q, p, idx, count, n_cap, keys, append, k_new, v_new, s);
+  return c.D == 128 ? launch_select_t<float, 128>(c, q, p, idx, count, n_cap, keys, append, k_new, v_new, s)
+                    : launch_select_t<float, 64>(c, q, p, idx, count, n_cap, keys, append, k_new, v_new, s);
 }
 }  // namespace
 

@@ -16,6 +16,10 @@ constexpr int kTopnMaxPerThread = 32;   // => at most 32768 blocks per sequence
 constexpr int kRectTileKeys = 32;       // keys per MFMA key tile
 constexpr int kMaxRectF = 1024;
 
+// Row stride (in keys) of the selection workspace: max_blocks_per_seq rounded
+// up to even, so every row starts on 16 bytes.
+__host__ __device__ constexpr int key_stride(int maxb) { return (maxb + 1) & ~1; }
+
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -39,6 +43,19 @@ constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141;   // reverse within each group of 8 lanes
 constexpr int kDppRowMirror = 0x140;    // reverse within each row of 16 lanes
+constexpr int kDppRowShr1 = 0x111;      // row_shr:1 (row_shr:n is 0x110 + n)
+constexpr int kDppRowBcast15 = 0x142;   // lane 15 of each row to the whole next row
+constexpr int kDppRowBcast31 = 0x143;   // lane 31 to rows 2 and 3
+
+// Operand types of the direct global-to-LDS load builtin.
+typedef __attribute__((address_space(1))) const void* global_ptr_t;
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Wait until at most N vector-memory instructions of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt(((N >> 4) & 3) << 14 | (0xF << 8) | (7 << 4) | (N & 15));
+}
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float x) {
