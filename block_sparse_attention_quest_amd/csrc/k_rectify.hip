@@ -219,8 +219,9 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 // grid: x = workgroup range of the plan (slots); NWV waves. In an item of row
 // tile rt, wave w owns query rows 32 (NWV rt + w) .. + 31 (a wave past the G * f
-// rows only loads). NS tile stages.
-template <int D, int NWV, int NS>
+// rows only loads). NS tile stages. CPOL is the cache policy of the K/V tile
+// loads (0, or kCachePolicyNT to stream them past the caches).
+template <int D, int NWV, int NS, int CPOL>
 __global__ __launch_bounds__(64 * NWV, 2) void k_rect_mfma(RectArgs a) {
   constexpr int NT = 64 * NWV;
   constexpr int KSTEPS = D / 16;   // 16-deep k-steps of the score product
@@ -327,7 +328,7 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_rect_mfma(RectArgs a) {
         const bool isk = LPT >= 2 ? li < LPT / 2 : ld_k[li];
         const char* src = (isk ? kbase : vbase) + size_t(page) * pstride + ld_off[li];
         uint4* dst = (isk ? kst : vst) + ld_dst[li];
-        __builtin_amdgcn_global_load_lds((global_ptr_t)src, (lds_ptr_t)dst, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((global_ptr_t)src, (lds_ptr_t)dst, 16, 0, CPOL);
       }
     };
 
@@ -665,8 +666,11 @@ __global__ __launch_bounds__(64) void k_rect_valu(RectArgs a, void* __restrict__
 }
 
 template <int D, int NWV, int NS>
-hipError_t launch_mfma_t(const RectArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((k_rect_mfma<D, NWV, NS>), dim3(a.slots), dim3(64 * NWV), 0, st, a);
+hipError_t launch_mfma_t(const RectArgs& a, bool stream, hipStream_t st) {
+  if (stream)
+    hipLaunchKernelGGL((k_rect_mfma<D, NWV, NS, kCachePolicyNT>), dim3(a.slots), dim3(64 * NWV), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_rect_mfma<D, NWV, NS, 0>), dim3(a.slots), dim3(64 * NWV), 0, st, a);
   return hipGetLastError();
 }
 
@@ -676,7 +680,15 @@ hipError_t launch_mfma(const RectArgs& a, void* out, hipStream_t st) {
   hipLaunchKernelGGL(k_rect_plan, dim3(1), dim3(kPlanThreads), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = a.tile_rows == 128 ? launch_mfma_t<D, 4, 4>(a, st) : launch_mfma_t<D, 8, 8>(a, st);
+  // The K/V a call may read: when it is larger than the last-level cache, no
+  // later call can find it there, so the tiles stream past the caches and leave
+  // them to the block descriptors (the periodic rectification of long contexts:
+  // 414 -> 395 us at 128K, batch 4); when it fits, the next call over the same
+  // prefix (the next prefill chunk) reads it from there (streaming it cost the
+  // 32K chunked prefill 9%).
+  const size_t kv_bytes = size_t(c.B) * c.Hkv * c.max_seq_len * 2 * D * sizeof(uint16_t);
+  const bool stream = kv_bytes > kLastLevelCacheBytes;
+  e = a.tile_rows == 128 ? launch_mfma_t<D, 4, 4>(a, stream, st) : launch_mfma_t<D, 8, 8>(a, stream, st);
   if (e != hipSuccess) return e;
   dim3 g2((a.rows + 3) / 4, c.Hkv, c.B);
   hipLaunchKernelGGL((k_rect_combine<uint16_t, D>), g2, dim3(256), 0, st, a, out);

@@ -15,6 +15,8 @@ constexpr int kTopnThreads = 1024;      // one workgroup per (sequence, KV head)
 constexpr int kTopnMaxPerThread = 32;   // => at most 32768 blocks per sequence
 constexpr int kRectTileKeys = 32;       // keys per MFMA key tile
 constexpr int kMaxRectF = 1024;
+constexpr size_t kLastLevelCacheBytes = size_t(256) << 20;  // MI355X Infinity Cache
+constexpr int kCachePolicyNT = 2;  // cache-policy operand of the direct-to-LDS load: non-temporal
 
 // Row stride (in keys) of the selection workspace: max_blocks_per_seq rounded
 // up to even, so every row starts on 16 bytes.
