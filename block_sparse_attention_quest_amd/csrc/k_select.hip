@@ -34,6 +34,8 @@
 // The two kernels hand over through the workspace at the kernel boundary: a
 // cross-workgroup hand-off inside one kernel would need device-scope fences,
 // which write back and invalidate a whole L2 on this multi-die part.
+#include <type_traits>
+
 #include "refresh_block.h"
 
 namespace resa {
@@ -398,36 +400,51 @@ __device__ __forceinline__ void topn_row(const Keys& keys, TopnShared& sm, int M
   int wcount = 0;  // wave-uniform
   // (key & mask) > prefix  <=>  key > prefix | ~mask;  (key & mask) >= prefix  <=>  key >= prefix
   const uint64_t top = prefix | ~mask;
-  const bool any = mode != 0, take_eq = mode == 1;
-  keys.each([&](int j, uint64_t key) {
-    const bool cand = j < Mo;
-    const bool gt = key > top, ge = key >= prefix;
-    const bool s = (cand & any & (gt | (ge & take_eq))) | (!cand & (j < M));
-    const bool at = cand & ge & !gt;
-    const uint64_t bs = __builtin_amdgcn_ballot_w64(s);
-    const int w0 = (j - lane) >> 5;
-    if (lane == 0) {
-      sm.u.a.sel[w0] = uint32_t(bs);
-      sm.u.a.sel[w0 + 1] = uint32_t(bs >> 32);
-    }
-    if (mode >= 2) {
-      const uint64_t bt = __builtin_amdgcn_ballot_w64(at);
-      if (mode == 2) {  // the tie words are read in mode 2 only
+  // one loop per mode, so that every test in it is a per-lane comparison
+  auto mark = [&](auto mode_c) {
+    constexpr int MODE = decltype(mode_c)::value;
+    keys.each([&](int j, uint64_t key) {
+      const bool cand = j < Mo, forced = !cand && j < M;
+      bool s = forced, at = false;
+      if constexpr (MODE == 1) s = (cand && key >= prefix) || forced;
+      if constexpr (MODE >= 2) {
+        const bool gt = key > top;
+        s = (cand && gt) || forced;
+        at = cand && !gt && key >= prefix;
+      }
+      const uint64_t bs = __builtin_amdgcn_ballot_w64(s);
+      const int w0 = (j - lane) >> 5;
+      if (lane == 0) {
+        sm.u.a.sel[w0] = uint32_t(bs);
+        sm.u.a.sel[w0 + 1] = uint32_t(bs >> 32);
+      }
+      if constexpr (MODE == 2) {  // the tie words are read in mode 2 only
+        const uint64_t bt = __builtin_amdgcn_ballot_w64(at);
         if (lane == 0) {
           sm.u.a.tie[w0] = uint32_t(bt);
           sm.u.a.tie[w0 + 1] = uint32_t(bt >> 32);
         }
-      } else if (bt) {
-        if (at) {
-          const int slot = wcount + int(__builtin_amdgcn_mbcnt_hi(uint32_t(bt >> 32),
-                                                                  __builtin_amdgcn_mbcnt_lo(uint32_t(bt), 0u)));
-          sm.u.a.gk[wave][slot] = key;
-          sm.u.a.gj[wave][slot] = j;
-        }
-        wcount += __builtin_popcountll(bt);
       }
-    }
-  });
+      if constexpr (MODE == 3) {
+        const uint64_t bt = __builtin_amdgcn_ballot_w64(at);
+        if (bt) {
+          if (at) {
+            const int slot = wcount + int(__builtin_amdgcn_mbcnt_hi(uint32_t(bt >> 32),
+                                                                    __builtin_amdgcn_mbcnt_lo(uint32_t(bt), 0u)));
+            sm.u.a.gk[wave][slot] = key;
+            sm.u.a.gj[wave][slot] = j;
+          }
+          wcount += __builtin_popcountll(bt);
+        }
+      }
+    });
+  };
+  switch (mode) {
+    case 0: mark(std::integral_constant<int, 0>{}); break;
+    case 1: mark(std::integral_constant<int, 1>{}); break;
+    case 2: mark(std::integral_constant<int, 2>{}); break;
+    default: mark(std::integral_constant<int, 3>{}); break;
+  }
   if (mode == 3 && lane == 0) sm.gcount[wave] = wcount;
   __syncthreads();
   if (mode == 3 && wave == 0) {
