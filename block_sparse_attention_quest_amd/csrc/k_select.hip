@@ -260,6 +260,7 @@ struct alignas(16) TopnShared {
   int gcount[kTopnWaves];
   int digit, k_rem, gsize;
 };
+
 // Keys in registers: EMAX per thread, block j = e * 1024 + tid, all loads
 // issued together (slots past the row re-read entry 0 and are ignored). The
 // per-block steps are unrolled over the EMAX registers.
