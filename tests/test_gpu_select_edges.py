@@ -11,7 +11,8 @@ The cases drive each branch of the selection: all scores equal, many exact
 ties, keys that differ only in their low 32 bits, a threshold group of up to
 64 blocks ranked one by one (and one of 70, which needs another radix pass),
 a top group that fills the quota exactly, signed zeros and negative scores,
-with n_local 0, 1 and 4 and rows of 1 to 5 register keys per thread.
+with n_local 0, 1 and 4 and rows of 1 to 5 register keys per thread, and
+rows of 18 and 32 keys per thread (288K and 512K tokens, the longest rows).
 """
 
 import numpy as np
@@ -65,7 +66,7 @@ def _run(kind, lens, params, q0=1.0, q1=0.0, group=60, Hkv=2, G=4, d=64, seed=0)
     rng = np.random.default_rng(seed)
     B = len(lens)
     Ms = [O.num_blocks(L) for L in lens]
-    maxb = max(Ms) + 2
+    maxb = min(max(Ms) + 2, 32768)  # the library's limit on blocks per sequence
     pages_needed = sum(Ms)
     Pn = pages_needed + 3
     perm = rng.permutation(Pn)
@@ -139,3 +140,10 @@ def test_select_threshold_group_size(group):
 def test_select_short_rows(kind):
     q1 = TINY if kind != "integer_ties" else 0.0
     _run(kind, LENS_B, (16, 0.1, 1), 1.0, q1, seed=7)
+
+
+@pytest.mark.parametrize("kind", ["integer_ties", "ranked_group", "low_word"])
+@pytest.mark.parametrize("lens", [[18000 * 16 + 5, 7000], [32768 * 16, 16 * 20000 + 3]], ids=["18_keys", "32_keys"])
+def test_select_long_rows(kind, lens):
+    q1 = 0.0 if kind == "integer_ties" else TINY
+    _run(kind, lens, (16, 0.1, 1), 1.0, q1, Hkv=1, seed=11)
