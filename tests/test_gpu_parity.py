@@ -93,6 +93,11 @@ SMALL = [
     ("bf16_dense_r1", "bf16", 2, 8, 2, 128, (100, 31), 5, 5, 1, 1.0, 1),
     ("bf16_no_local", "bf16", 2, 8, 2, 128, (600, 17), 6, 3, 4, 0.05, 0),
     ("bf16_nmin_over_M", "bf16", 2, 8, 2, 128, (40, 200), 4, 2, 64, 0.1, 1),
+    ("bf16_g8_d64", "bf16", 2, 16, 2, 64, (700, 45), 6, 20, 8, 0.1, 1),   # 160 rectified rows: 256-row tiles
+    ("bf16_g1_d64", "bf16", 2, 2, 2, 64, (300, 1200), 5, 5, 4, 0.1, 1),
+    ("fp32_g8_d64", "fp32", 1, 16, 2, 64, (900,), 5, 5, 8, 0.1, 1),
+    ("fp32_g2_d128", "fp32", 2, 4, 2, 128, (150, 420), 6, 3, 4, 0.2, 2),
+    ("fp32_g1_d64", "fp32", 2, 2, 2, 64, (64, 257), 4, 4, 2, 0.25, 0),
 ]
 
 
