@@ -258,3 +258,58 @@ def test_decode_is_deterministic():
         outs.append(res)
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+
+
+def test_calls_from_two_host_threads_on_two_streams():
+    """The library keeps no mutable state but the thread-local error text: two
+    host threads, each with its own stream, workspace and outputs, select and
+    decode over one shared cache concurrently; both results equal a
+    single-threaded call's bit for bit, and an error raised on one thread does
+    not show in the other's message."""
+    import threading
+    from block_sparse_attention_quest_amd import resa as R
+    w = W.Workload("threads", "bf16", 3, 8, 2, 128, (5000, 1234, 777), 2, 0, 16, 0.1, 1, (5, 5, 5), True, 21)
+    r = _runner(w)
+    q = W.query(w, 0).cuda()
+    r.set_step_lens(0)
+    ws_size = max(R.resa_select_workspace_size(r.cache), R.resa_decode_workspace_size(r.cache, r.n_cap))
+
+    def call(stream):
+        ws = R.workspace(ws_size)
+        idx = torch.full_like(r.idx, -1)
+        count = torch.zeros_like(r.count)
+        out = torch.empty_like(r.out)
+        stream.wait_stream(torch.cuda.current_stream())  # the fills above run on this thread's current stream
+        with torch.cuda.stream(stream):
+            R.resa_select_blocks(r.cache, q, r.params, idx, count, r.n_cap, ws, stream)
+            R.resa_sparse_decode(r.cache, q, idx, count, r.n_cap, out, ws, r.scale, stream)
+        stream.synchronize()
+        return idx, count, out
+
+    ref = call(torch.cuda.current_stream())
+    results, errors = {}, {}
+
+    def worker(i):
+        try:
+            s = torch.cuda.Stream()
+            results[i] = [call(s) for _ in range(4)]
+            if i == 1:  # a rejected call on this thread only
+                try:
+                    R.resa_sparse_decode(r.cache, q, r.idx, r.count, 0, r.out, r.ws)
+                except R.ResaError:
+                    errors[i] = R.load().resa_last_error().decode()
+            else:
+                errors[i] = R.load().resa_last_error().decode()
+        except Exception as e:  # reported by the main thread
+            errors[i] = repr(e)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert "n_cap" in errors[1], errors
+    assert errors[0] == "", errors
+    for i in range(2):
+        for idx, count, out in results[i]:
+            assert torch.equal(idx, ref[0]) and torch.equal(count, ref[1]) and torch.equal(out, ref[2])
