@@ -526,7 +526,7 @@ def main():
                "decode": 1e3 * sum(e[2].elapsed_time(e[3]) for e in cold_ev) / COLD_REPS - pair_us}
     del flush, sink
 
-    # ---- a plain device copy of 1 GiB (read + write), the box's own
+    # ---- a plain device copy of 1 GiB (read + write), this GPU's own
     # streaming reference beside the published peak ----
     src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
