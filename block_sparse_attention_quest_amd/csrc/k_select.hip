@@ -249,6 +249,8 @@ struct TopnAfter {
   uint32_t tie[kBitmapWords];
   uint64_t gk[kTopnWaves][kRankGroup];  // ranked group: each wave's members in its own order
   int gj[kTopnWaves][kRankGroup];
+  uint64_t ck[kRankGroup];  // the ranked group laid end to end
+  int cj[kRankGroup];
 };
 struct alignas(16) TopnShared {
   union {
@@ -449,9 +451,9 @@ __device__ __forceinline__ void topn_row(const Keys& keys, TopnShared& sm, int M
   if (mode == 3 && lane == 0) sm.gcount[wave] = wcount;
   __syncthreads();
   if (mode == 3 && wave == 0) {
-    // ranked group (key descending, index ascending; usually a handful of
-    // blocks): member i in lane i (the waves' lists laid end to end), then
-    // every member counts the members that come before it
+    // ranked group (key descending, index ascending; a few dozen blocks at
+    // most): member i in lane i (the waves' lists laid end to end), then every
+    // member counts the members that come before it
     const int incl = row_incl_scan(lane < kTopnWaves ? sm.gcount[lane] : 0);
     const int gs = __builtin_amdgcn_readlane(incl, kTopnWaves - 1);
     int owner = 0, base = 0;
@@ -469,13 +471,17 @@ __device__ __forceinline__ void topn_row(const Keys& keys, TopnShared& sm, int M
       kt = sm.u.a.gk[owner][lane - base];
       jt = sm.u.a.gj[owner][lane - base];
     }
-    const uint32_t klo = uint32_t(kt), khi = uint32_t(kt >> 32);
+    // the group goes to LDS once, then every member is read back as a
+    // broadcast (one address for the whole wave), several in flight at once;
+    // the same wave writes and reads, so program order makes the writes visible
+    sm.u.a.ck[lane] = kt;
+    sm.u.a.cj[lane] = jt;
     int rank = 0;
+#pragma unroll 8
     for (int u = 0; u < gs; ++u) {
-      const uint64_t ku = (uint64_t(uint32_t(__builtin_amdgcn_readlane(khi, u))) << 32) |
-                          uint32_t(__builtin_amdgcn_readlane(klo, u));
-      const int ju = __builtin_amdgcn_readlane(jt, u);
-      rank += (ku > kt || (ku == kt && ju < jt)) ? 1 : 0;
+      const uint64_t ku = sm.u.a.ck[u];
+      const int ju = sm.u.a.cj[u];
+      rank += int(ku > kt) | (int(ku == kt) & int(ju < jt));  // no short circuit: both loads issue
     }
     if (lane < gs && rank < k) atomicOr(&sm.u.a.sel[jt >> 5], 1u << (jt & 31));
   }
