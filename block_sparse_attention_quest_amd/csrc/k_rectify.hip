@@ -10,7 +10,8 @@
 // (one wave per 32 rows); a row tile needs the keys up to the last position its
 // last row sees. The key ranges of all (sequence, KV head, row tile) segments,
 // laid end to end in tiles of 32 keys, are cut into one equal range per
-// workgroup (the work plan, k_rect_plan), so a mixed-length batch still fills
+// workgroup (the work plan, built by one workgroup of the first launch,
+// k_rect_prep, beside the write and refresh), so a mixed-length batch still fills
 // the chip evenly; a range that crosses from one segment into the next becomes
 // two work items with a partial each. For an item the K/V tiles stream from HBM
 // into LDS once and serve all G * f rows (HBM traffic is the cache once per
@@ -28,12 +29,11 @@
 // fp32 path (k_rect_valu): one wave per (sequence, row, head), plain VALU.
 #include <type_traits>
 
-#include "resa_internal.h"
+#include "refresh_block.h"
 
 namespace resa {
 namespace {
 
-constexpr int kPlanThreads = 1024;
 constexpr int kMaxItemTiles = 1024;  // tiles per workgroup range (32768 keys)
 
 struct RectArgs {
@@ -57,6 +57,7 @@ __device__ __forceinline__ long long ceil_div_ll(long long x, long long y) { ret
 
 // Exclusive prefix sum over the workgroup (wave shuffles, then one pass over
 // the wave totals); *total gets the sum of all values.
+template <int NT>
 __device__ long long block_exclusive_scan(long long v, long long* sh, long long* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   long long x = v;
@@ -69,7 +70,7 @@ __device__ long long block_exclusive_scan(long long v, long long* sh, long long*
   __syncthreads();
   long long before = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < kPlanThreads / 64; ++w) {
+  for (int w = 0; w < NT / 64; ++w) {
     const long long t = sh[w];
     before += w < wave ? t : 0;
     tot += t;
@@ -92,9 +93,11 @@ __device__ long long block_exclusive_scan(long long v, long long* sh, long long*
 // are lo(w) for w in [ceil((a+1) P / TT), ceil(e P / TT) - 1]. Threads take
 // contiguous runs of sequences, then of segments; consecutive boundaries are
 // stepped without division (lo(w) = w q + floor(w r / P), TT = q P + r).
-__global__ __launch_bounds__(kPlanThreads) void k_rect_plan(RectArgs a) {
+// NT threads of one workgroup build the plan.
+template <int NT>
+__device__ __forceinline__ void rect_plan(const RectArgs& a) {
   const CacheView& c = a.c;
-  __shared__ long long sh[kPlanThreads / 64];
+  __shared__ long long sh[NT / 64];
   const int tid = threadIdx.x;
   const long long Hkv = c.Hkv;
   const int RT = a.rtiles;
@@ -110,12 +113,12 @@ __global__ __launch_bounds__(kPlanThreads) void k_rect_plan(RectArgs a) {
     return t;
   };
 
-  const int per_b = (c.B + kPlanThreads - 1) / kPlanThreads;
+  const int per_b = (c.B + NT - 1) / NT;
   const int b0 = min(c.B, tid * per_b), b1 = min(c.B, b0 + per_b);
   long long tloc = 0;
   for (int b = b0; b < b1; ++b) tloc += tiles(b);
   long long tsum;
-  long long pt = block_exclusive_scan(tloc, sh, &tsum);
+  long long pt = block_exclusive_scan<NT>(tloc, sh, &tsum);
   for (int b = b0; b < b1; ++b) {
     a.ptile[b] = pt;
     pt += tiles(b);
@@ -128,7 +131,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_rect_plan(RectArgs a) {
   __syncthreads();  // ptile visible to the workgroup
 
   const int S = c.B * c.Hkv * RT;
-  const int per_s = (S + kPlanThreads - 1) / kPlanThreads;
+  const int per_s = (S + NT - 1) / NT;
   const int s0 = min(S, tid * per_s), s1 = min(S, s0 + per_s);
   // segment s: first tile, end tile, and the range starts strictly inside
   auto segment = [&](int s, long long& as, long long& es, long long& wl, long long& wh) {
@@ -148,7 +151,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_rect_plan(RectArgs a) {
     cloc += 1 + (wh >= wl ? wh - wl + 1 : 0);
   }
   long long nitems;
-  long long fi = block_exclusive_scan(cloc, sh, &nitems);
+  long long fi = block_exclusive_scan<NT>(cloc, sh, &nitems);
   for (int s = s0; s < s1; ++s) {
     long long as, es, wl, wh;
     segment(s, as, es, wl, wh);
@@ -176,7 +179,28 @@ __global__ __launch_bounds__(kPlanThreads) void k_rect_plan(RectArgs a) {
     }
     fi += cnt;
   }
-  for (long long w = P + tid; w <= a.slots; w += kPlanThreads) a.wg_first[w] = int(nitems);
+  for (long long w = P + tid; w <= a.slots; w += NT) a.wg_first[w] = int(nitems);
+}
+
+// The first launch of a bf16 rectification: the write of the f rectified rows
+// and the refresh of their blocks' descriptors (one wave per (block slot, KV
+// head, sequence), as resa_update_descriptors does), with the work plan built
+// by one more workgroup, the first of an extra x column (the plan reads only
+// the lengths, so the two are independent). grid (slots + 1, Hkv, B), 64
+// threads.
+template <typename T, int D>
+__global__ __launch_bounds__(64) void k_rect_prep(RectArgs a, const void* __restrict__ k_new,
+                                                  const void* __restrict__ v_new) {
+  if (blockIdx.x == gridDim.x - 1) {
+    if (blockIdx.y == 0 && blockIdx.z == 0) rect_plan<64>(a);
+    return;
+  }
+  const CacheView& c = a.c;
+  const int b = blockIdx.z, g = blockIdx.y, lane = threadIdx.x;
+  const int L = c.seq_lens[b];
+  const int j = max(0, L - a.f) / kBlock + blockIdx.x;
+  if (j * kBlock >= L) return;
+  refresh_block<T, D>(c, k_new, v_new, a.f, b, g, j, L, lane);
 }
 
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -675,9 +699,10 @@ hipError_t launch_mfma_t(const RectArgs& a, bool stream, hipStream_t st) {
 }
 
 template <int D>
-hipError_t launch_mfma(const RectArgs& a, void* out, hipStream_t st) {
+hipError_t launch_mfma(const RectArgs& a, const void* k_new, const void* v_new, void* out, hipStream_t st) {
   const CacheView& c = a.c;
-  hipLaunchKernelGGL(k_rect_plan, dim3(1), dim3(kPlanThreads), 0, st, a);
+  const int slots = (a.f + kBlock - 1) / kBlock + 1;  // blocks a range of f positions can touch
+  hipLaunchKernelGGL((k_rect_prep<uint16_t, D>), dim3(slots + 1, c.Hkv, c.B), dim3(64), 0, st, a, k_new, v_new);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // The K/V a call may read: when it is larger than the last-level cache, no
@@ -727,8 +752,8 @@ size_t rectify_ws_bytes(const CacheView& c, int f) {
   return plan_bytes(c, p) + align_up(slots * 2 * sizeof(float), 256) + slots * c.D * sizeof(float);
 }
 
-hipError_t launch_rectify_attention(const CacheView& c, const void* q, int f, float scale, void* out,
-                                    void* ws, hipStream_t st) {
+hipError_t launch_rectify(const CacheView& c, const void* q, const void* k_new, const void* v_new, int f,
+                          float scale, void* out, void* ws, hipStream_t st) {
   const RectPlan p = plan_rectify(c, f);
   RectArgs a;
   a.c = c;
@@ -753,7 +778,11 @@ hipError_t launch_rectify_attention(const CacheView& c, const void* q, int f, fl
   const size_t slots = size_t(p.cap) * p.rows_pad;
   a.part_ml = reinterpret_cast<float*>(w);
   a.part_acc = reinterpret_cast<float*>(w + align_up(slots * 2 * sizeof(float), 256));
-  if (c.dtype == RESA_BF16) return c.D == 128 ? launch_mfma<128>(a, out, st) : launch_mfma<64>(a, out, st);
+  if (c.dtype == RESA_BF16)
+    return c.D == 128 ? launch_mfma<128>(a, k_new, v_new, out, st) : launch_mfma<64>(a, k_new, v_new, out, st);
+  // fp32: the write and refresh, then the plain rows
+  const hipError_t e = launch_update_tail(c, k_new, v_new, f, st);
+  if (e != hipSuccess) return e;
   dim3 grid(c.Hq, f, c.B);
   if (c.D == 128)
     hipLaunchKernelGGL((k_rect_valu<float, 128>), grid, dim3(64), 0, st, a, out);

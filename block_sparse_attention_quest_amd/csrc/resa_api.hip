@@ -183,11 +183,10 @@ resa_status resa_rectify(const resa_cache* cache, const void* q, const void* k_n
   if (!(scale > 0.f) || !isfinite(scale)) return fail(RESA_ERR_INVALID, "scale must be positive and finite");
   const size_t need = resa::rectify_ws_bytes(v, f);
   if (!ws || ws_bytes < need) return fail(RESA_ERR_WORKSPACE, "rectify workspace %zu < %zu bytes", ws_bytes, need);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  // order matters: rectified rows attend to the rectified K/V of earlier rows
-  hipError_t e = resa::launch_update_tail(v, k_new, v_new, f, s);
-  if (e != hipSuccess) return hip_status(e, "resa_rectify (write + refresh)");
-  return hip_status(resa::launch_rectify_attention(v, q, f, scale, out, ws, s), "resa_rectify");
+  // the write and refresh come first: rectified rows attend to the rectified
+  // K/V of earlier rows
+  return hip_status(resa::launch_rectify(v, q, k_new, v_new, f, scale, out, ws, static_cast<hipStream_t>(stream)),
+                    "resa_rectify");
 }
 
 const char* resa_last_error(void) { return g_err; }

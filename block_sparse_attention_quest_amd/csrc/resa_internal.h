@@ -122,8 +122,10 @@ struct RectPlan {
 };
 RectPlan plan_rectify(const CacheView& c, int f);
 size_t rectify_ws_bytes(const CacheView& c, int f);
-hipError_t launch_rectify_attention(const CacheView& c, const void* q, int f, float scale, void* out,
-                                    void* ws, hipStream_t s);
+// The whole rectification: write the f rows and refresh their blocks, then the
+// causal rows (the first launch also builds the bf16 path's work plan).
+hipError_t launch_rectify(const CacheView& c, const void* q, const void* k_new, const void* v_new, int f,
+                          float scale, void* out, void* ws, hipStream_t s);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
