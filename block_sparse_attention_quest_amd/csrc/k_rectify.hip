@@ -1,8 +1,8 @@
 // Dense rectification attention (Pith review of "Rectified Sparse Attention",
 // "What carries the argument" and "The reading"): after the f newest positions
-// of every sequence have been overwritten with their re-encoded K/V (done by the
-// descriptor kernel on the same stream), row i of every query head attends
-// causally over the whole cache, positions 0 .. L - f + i.
+// of every sequence have been overwritten with their re-encoded K/V and their
+// blocks' descriptors refreshed (the first launch of the call), row i of every
+// query head attends causally over the whole cache, positions 0 .. L - f + i.
 //
 // bf16 path (k_rect_mfma): per KV head the G * f query rows form one dense
 // contraction against every key, so it runs on the matrix cores
@@ -15,7 +15,8 @@
 // the chip evenly; a range that crosses from one segment into the next becomes
 // two work items with a partial each. For an item the K/V tiles stream from HBM
 // into LDS once and serve all G * f rows (HBM traffic is the cache once per
-// event, not once per head). Each wave owns a 32-row tile of queries, kept in
+// event, not once per head); when the K/V the call may read exceeds the
+// last-level cache, the tile loads are non-temporal. Each wave owns a 32-row tile of queries, kept in
 // registers. Scores are computed transposed, S^T = K Q^T, so a lane holds 16
 // keys of one query row and the probabilities feed O^T = V^T P^T as its B
 // operand with no data movement. The rows of a K tile are stored in LDS in an
