@@ -617,14 +617,36 @@ __global__ __launch_bounds__(256) void k_rect_combine(RectArgs a, void* __restri
   float num[D / 64], den = 0.f;
 #pragma unroll
   for (int e = 0; e < D / 64; ++e) num[e] = 0.f;
-  for (int sp = 0; sp < live; ++sp) {
-    const size_t slot = (size_t(gr.x) + sp) * a.rows_pad + r;
-    const float ms = a.part_ml[slot * 2];
-    const float w = ms == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(ms - mx);
-    den = fmaf(w, a.part_ml[slot * 2 + 1], den);
+  // Rows with many items (short ranges: the chunks of a prefill) request the
+  // partials in batches of 16 before any is used, one round trip per batch
+  // (past the last item: the last one again, unused); rows with a few items
+  // take them one by one, which measured faster there than idle batch slots.
+  auto merge = [&](auto batch_c) {
+    constexpr int BATCH = decltype(batch_c)::value;
+    for (int sp0 = 0; sp0 < live; sp0 += BATCH) {
+      float ms[BATCH], ls[BATCH], av[BATCH][D / 64];
 #pragma unroll
-    for (int e = 0; e < D / 64; ++e) num[e] = fmaf(w, a.part_acc[slot * D + lane + 64 * e], num[e]);
-  }
+      for (int u = 0; u < BATCH; ++u) {
+        const size_t slot = (size_t(gr.x) + min(sp0 + u, live - 1)) * a.rows_pad + r;
+        ms[u] = a.part_ml[slot * 2];
+        ls[u] = a.part_ml[slot * 2 + 1];
+#pragma unroll
+        for (int e = 0; e < D / 64; ++e) av[u][e] = a.part_acc[slot * D + lane + 64 * e];
+      }
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        if (sp0 + u >= live) break;  // wave-uniform
+        const float w = ms[u] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(ms[u] - mx);
+        den = fmaf(w, ls[u], den);
+#pragma unroll
+        for (int e = 0; e < D / 64; ++e) num[e] = fmaf(w, av[u][e], num[e]);
+      }
+    }
+  };
+  if (live > 4)
+    merge(std::integral_constant<int, 16>{});
+  else
+    merge(std::integral_constant<int, 1>{});
   const int i = R / c.G, h = R % c.G;
   const float inv = 1.f / den;
   const size_t o0 = ((size_t(b) * a.f + i) * c.Hq + size_t(g) * c.G + h) * D;
