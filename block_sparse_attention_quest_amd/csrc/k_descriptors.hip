@@ -16,8 +16,9 @@ namespace resa {
 namespace {
 
 // blockIdx: x = block slot within the refreshed range, y = KV head, z = sequence.
-// n_new == 0: rebuild (slot = logical block index, nothing written).
-template <typename T, int D>
+// n_new == 0: rebuild (slot = logical block index, nothing written). NEW: rows
+// come from k_new / v_new (false when the caller passes none).
+template <typename T, int D, bool NEW>
 __global__ __launch_bounds__(64) void k_refresh_blocks(CacheView c, const void* __restrict__ k_new,
                                                        const void* __restrict__ v_new, int n_new) {
   const int b = blockIdx.z, g = blockIdx.y, lane = threadIdx.x;
@@ -25,7 +26,7 @@ __global__ __launch_bounds__(64) void k_refresh_blocks(CacheView c, const void* 
   const int lo = n_new > 0 ? max(0, L - n_new) : 0;
   const int j = lo / kBlock + blockIdx.x;
   if (j * kBlock >= L) return;
-  refresh_block<T, D>(c, k_new, v_new, n_new, b, g, j, L, lane);
+  refresh_block<T, D, NEW>(c, k_new, v_new, n_new, b, g, j, L, lane);
 }
 
 template <typename T, int D>
@@ -33,7 +34,10 @@ hipError_t launch_refresh_t(const CacheView& c, const void* k_new, const void* v
                             hipStream_t s) {
   const int slots = n_new > 0 ? (n_new + kBlock - 1) / kBlock + 1 : c.maxb;
   dim3 grid(slots, c.Hkv, c.B);
-  hipLaunchKernelGGL((k_refresh_blocks<T, D>), grid, dim3(64), 0, s, c, k_new, v_new, n_new);
+  if (n_new > 0 && k_new != nullptr)
+    hipLaunchKernelGGL((k_refresh_blocks<T, D, true>), grid, dim3(64), 0, s, c, k_new, v_new, n_new);
+  else
+    hipLaunchKernelGGL((k_refresh_blocks<T, D, false>), grid, dim3(64), 0, s, c, k_new, v_new, n_new);
   return hipGetLastError();
 }
 

@@ -10,20 +10,42 @@
 
 namespace resa {
 
-template <typename T>
+// A lane's CPL consecutive elements of a row, as one vector access (the row
+// offset i is a multiple of CPL).
+template <typename T, int CPL>
 struct Elem;
-template <>
-struct Elem<float> {
-  __device__ static float load(const void* p, size_t i) { return static_cast<const float*>(p)[i]; }
-  __device__ static void store(void* p, size_t i, float x) { static_cast<float*>(p)[i] = x; }
+template <int CPL>
+struct Elem<float, CPL> {
+  typedef float vec __attribute__((ext_vector_type(CPL)));
+  __device__ static void load(const void* p, size_t i, float* x) {
+    const vec v = *reinterpret_cast<const vec*>(static_cast<const float*>(p) + i);
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) x[e] = v[e];
+  }
+  __device__ static void store(void* p, size_t i, const float* x) {
+    vec v;
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) v[e] = x[e];
+    *reinterpret_cast<vec*>(static_cast<float*>(p) + i) = v;
+  }
+  __device__ static void store1(void* p, size_t i, float x) { static_cast<float*>(p)[i] = x; }
 };
-template <>
-struct Elem<uint16_t> {  // bf16 bits
-  __device__ static float load(const void* p, size_t i) {
-    return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
+template <int CPL>
+struct Elem<uint16_t, CPL> {  // bf16 bits
+  typedef uint16_t vec __attribute__((ext_vector_type(CPL)));
+  __device__ static void load(const void* p, size_t i, float* x) {
+    const vec v = *reinterpret_cast<const vec*>(static_cast<const uint16_t*>(p) + i);
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) x[e] = bf16_to_f32(v[e]);
   }
   // Only ever stores values that came from bf16, so the conversion is exact.
-  __device__ static void store(void* p, size_t i, float x) {
+  __device__ static void store(void* p, size_t i, const float* x) {
+    vec v;
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) v[e] = uint16_t(__float_as_uint(x[e]) >> 16);
+    *reinterpret_cast<vec*>(static_cast<uint16_t*>(p) + i) = v;
+  }
+  __device__ static void store1(void* p, size_t i, float x) {
     static_cast<uint16_t*>(p)[i] = uint16_t(__float_as_uint(x) >> 16);
   }
 };
@@ -31,60 +53,77 @@ struct Elem<uint16_t> {  // bf16 bits
 // One wave (64 lanes) refreshes block j of sequence b, KV head g, whose
 // sequence holds L tokens. Rows of the range [L - n_new, L) come from k_new /
 // v_new ([B][n_new][Hkv][D]) when those are given, are stored into the page
-// first (K token-major, V channel-major) and enter the min/max directly. A
-// token row is read by the 64 lanes in one coalesced access (a lane owns D/64
-// channels); all 16 rows are loaded unconditionally (slots past the end re-read
-// slot 0 and are ignored) so they are in flight together.
-template <typename T, int D>
+// (K token-major, V channel-major) and enter the min/max directly; only older
+// rows are read from the page. A lane owns D/64 consecutive channels, so a
+// token row is one coalesced access of the wave. Every row load of the block
+// is issued before any is used: slots past the end read slot 0's source again
+// (a repeat leaves min and max unchanged), and the V rows are consumed by an
+// empty asm statement ahead of the stores so that the compiler cannot move
+// each row's load next to its conditional store.
+// NEW = false builds the variant that never takes rows from k_new (the caller
+// passes none), which keeps the per-row V registers out of it.
+template <typename T, int D, bool NEW = true>
 __device__ __forceinline__ void refresh_block(const CacheView& c, const void* __restrict__ k_new,
                                               const void* __restrict__ v_new, int n_new, int b, int g, int j,
                                               int L, int lane) {
   constexpr int CPL = D / 64;  // channels per lane
+  typedef Elem<T, CPL> E;
+  const int c0 = lane * CPL;
+  const bool has_new = NEW && n_new > 0 && k_new != nullptr;
   const int lo = n_new > 0 ? max(0, L - n_new) : 0;
   const int page = c.bt[size_t(b) * c.maxb + j];
   const int valid = min(kBlock, L - j * kBlock);
   const size_t row0 = (size_t(page) * c.Hkv + g) * kBlock;  // token-row index of slot 0
+  const int first_new = has_new ? lo - j * kBlock : kBlock;  // slot of the first fresh row
+  // new-token row of slot t (clamped into the sequence's rows of k_new)
+  auto new_row = [&](int t) {
+    const int i = min(max(j * kBlock + t - (L - n_new), 0), n_new - 1);
+    return (size_t(b) * n_new + i) * c.Hkv + g;
+  };
 
+  float kv[kBlock][CPL], vv[kBlock][CPL];
+#pragma unroll
+  for (int t = 0; t < kBlock; ++t) {
+    const int tt = t < valid ? t : 0;
+    if (tt >= first_new)
+      E::load(k_new, new_row(tt) * D + c0, kv[t]);
+    else
+      E::load(c.k, (row0 + tt) * D + c0, kv[t]);
+  }
+  if (has_new) {
+#pragma unroll
+    for (int t = 0; t < kBlock; ++t) E::load(v_new, new_row(t) * D + c0, vv[t]);
+#pragma unroll
+    for (int t = 0; t < kBlock; ++t)
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) asm volatile("" ::"v"(vv[t][e]));
+  }
   float mn[CPL], mx[CPL];
 #pragma unroll
   for (int e = 0; e < CPL; ++e) {
-    mn[e] = __builtin_inff();
-    mx[e] = -__builtin_inff();
+    mn[e] = kv[0][e];
+    mx[e] = kv[0][e];
   }
-  float kv[kBlock][CPL];
 #pragma unroll
-  for (int t = 0; t < kBlock; ++t)
-#pragma unroll
-    for (int e = 0; e < CPL; ++e)
-      kv[t][e] = Elem<T>::load(c.k, (row0 + (t < valid ? t : 0)) * D + lane + 64 * e);
-  const int first_new = n_new > 0 && k_new != nullptr ? lo - j * kBlock : kBlock;  // slot of the first fresh row
-#pragma unroll
-  for (int t = 0; t < kBlock; ++t) {
-    if (t >= valid) continue;
-    if (t >= first_new) {
-      const size_t src_row = (size_t(b) * n_new + (j * kBlock + t - (L - n_new))) * c.Hkv + g;
-#pragma unroll
-      for (int e = 0; e < CPL; ++e) {
-        const int ch = lane + 64 * e;
-        kv[t][e] = Elem<T>::load(k_new, src_row * D + ch);
-        Elem<T>::store(c.kw, (row0 + t) * D + ch, kv[t][e]);
-        // V tiles are channel-major: [page][head][channel][slot]
-        Elem<T>::store(c.vw, (row0 * D + size_t(ch) * kBlock) + t, Elem<T>::load(v_new, src_row * D + ch));
-      }
-    }
+  for (int t = 1; t < kBlock; ++t)
 #pragma unroll
     for (int e = 0; e < CPL; ++e) {
       mn[e] = fminf(mn[e], kv[t][e]);
       mx[e] = fmaxf(mx[e], kv[t][e]);
     }
+  if (has_new) {
+#pragma unroll
+    for (int t = 0; t < kBlock; ++t) {
+      if (t < first_new || t >= valid) continue;
+      E::store(c.kw, (row0 + t) * D + c0, kv[t]);
+      // V tiles are channel-major: [page][head][channel][slot]
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) E::store1(c.vw, row0 * D + size_t(c0 + e) * kBlock + t, vv[t][e]);
+    }
   }
   const size_t d0 = (size_t(page) * c.Hkv + g) * 2 * D;
-#pragma unroll
-  for (int e = 0; e < CPL; ++e) {
-    const int ch = lane + 64 * e;
-    Elem<T>::store(c.desc, d0 + ch, mn[e]);
-    Elem<T>::store(c.desc, d0 + D + ch, mx[e]);
-  }
+  E::store(c.desc, d0 + c0, mn);
+  E::store(c.desc, d0 + D + c0, mx);
 }
 
 }  // namespace resa

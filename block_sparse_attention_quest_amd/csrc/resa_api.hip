@@ -5,6 +5,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <initializer_list>
+
 #include "resa_internal.h"
 
 namespace {
@@ -22,6 +24,16 @@ resa_status fail(resa_status st, const char* fmt, ...) {
 resa_status hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return RESA_OK;
   return fail(RESA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; }
+
+// Element arrays are read with vector loads of up to 16 bytes, integer arrays
+// with 4-byte loads.
+resa_status check_aligned16(const char* what, std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (p && !aligned(p, 16)) return fail(RESA_ERR_INVALID, "%s must be 16-byte aligned", what);
+  return RESA_OK;
 }
 
 resa_status check_cache(const resa_cache* c, resa::CacheView* v) {
@@ -48,6 +60,10 @@ resa_status check_cache(const resa_cache* c, resa::CacheView* v) {
     return fail(RESA_ERR_UNSUPPORTED, "num_kv_heads * head_dim exceeds 4096");
   if (!c->k_pages || !c->v_pages || !c->desc || !c->block_table || !c->seq_lens)
     return fail(RESA_ERR_INVALID, "cache has a NULL pointer");
+  if (!aligned(c->k_pages, 16) || !aligned(c->v_pages, 16) || !aligned(c->desc, 16))
+    return fail(RESA_ERR_INVALID, "k_pages, v_pages and desc must be 16-byte aligned");
+  if (!aligned(c->block_table, 4) || !aligned(c->seq_lens, 4))
+    return fail(RESA_ERR_INVALID, "block_table and seq_lens must be 4-byte aligned");
   v->dtype = c->dtype;
   v->B = c->batch;
   v->Hq = c->num_q_heads;
@@ -118,6 +134,7 @@ resa_status resa_update_descriptors(const resa_cache* cache, const void* k_new, 
   if ((k_new == nullptr) != (v_new == nullptr)) return fail(RESA_ERR_INVALID, "k_new and v_new must both be set or both be NULL");
   if (n_new == 0 && k_new) return fail(RESA_ERR_INVALID, "a rebuild (n_new == 0) takes no new tokens");
   if (n_new > v.max_seq_len) return fail(RESA_ERR_INVALID, "n_new %d exceeds max_seq_len %d", n_new, v.max_seq_len);
+  if ((st = check_aligned16("k_new and v_new", {k_new, v_new})) != RESA_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = n_new == 0 ? resa::launch_rebuild(v, s) : resa::launch_update_tail(v, k_new, v_new, n_new, s);
   return hip_status(e, "resa_update_descriptors");
@@ -131,6 +148,8 @@ resa_status resa_select_blocks(const resa_cache* cache, const void* q, const res
   if (st != RESA_OK) return st;
   if ((st = check_params(params)) != RESA_OK) return st;
   if (!q || !idx || !count) return fail(RESA_ERR_INVALID, "q, idx and count must not be NULL");
+  if ((st = check_aligned16("q and ws", {q, ws})) != RESA_OK) return st;
+  if (!aligned(idx, 4) || !aligned(count, 4)) return fail(RESA_ERR_INVALID, "idx and count must be 4-byte aligned");
   const int need_cap = n_for((v.max_seq_len + resa::kBlock - 1) / resa::kBlock, params);
   if (n_cap < need_cap) return fail(RESA_ERR_INVALID, "n_cap %d is below resa_n_cap() = %d", n_cap, need_cap);
   const size_t need = resa::select_ws_bytes(v);
@@ -148,6 +167,8 @@ resa_status resa_append_select(const resa_cache* cache, const void* k_new, const
   if ((st = check_params(params)) != RESA_OK) return st;
   if ((k_new == nullptr) != (v_new == nullptr)) return fail(RESA_ERR_INVALID, "k_new and v_new must both be set or both be NULL");
   if (!q || !idx || !count) return fail(RESA_ERR_INVALID, "q, idx and count must not be NULL");
+  if ((st = check_aligned16("q, k_new, v_new and ws", {q, k_new, v_new, ws})) != RESA_OK) return st;
+  if (!aligned(idx, 4) || !aligned(count, 4)) return fail(RESA_ERR_INVALID, "idx and count must be 4-byte aligned");
   const int need_cap = n_for((v.max_seq_len + resa::kBlock - 1) / resa::kBlock, params);
   if (n_cap < need_cap) return fail(RESA_ERR_INVALID, "n_cap %d is below resa_n_cap() = %d", n_cap, need_cap);
   const size_t need = resa::select_ws_bytes(v);
@@ -164,6 +185,8 @@ resa_status resa_sparse_decode(const resa_cache* cache, const void* q, const int
   resa_status st = check_cache(cache, &v);
   if (st != RESA_OK) return st;
   if (!q || !idx || !count || !out) return fail(RESA_ERR_INVALID, "q, idx, count and out must not be NULL");
+  if ((st = check_aligned16("q, out and ws", {q, out, ws})) != RESA_OK) return st;
+  if (!aligned(idx, 4) || !aligned(count, 4)) return fail(RESA_ERR_INVALID, "idx and count must be 4-byte aligned");
   if (n_cap < 1 || n_cap > v.maxb) return fail(RESA_ERR_INVALID, "n_cap %d outside 1 .. max_blocks_per_seq", n_cap);
   if (!(scale > 0.f) || !isfinite(scale)) return fail(RESA_ERR_INVALID, "scale must be positive and finite");
   const size_t need = resa::decode_ws_bytes(v, n_cap);
@@ -178,6 +201,7 @@ resa_status resa_rectify(const resa_cache* cache, const void* q, const void* k_n
   resa_status st = check_cache(cache, &v);
   if (st != RESA_OK) return st;
   if (!q || !k_new || !v_new || !out) return fail(RESA_ERR_INVALID, "q, k_new, v_new and out must not be NULL");
+  if ((st = check_aligned16("q, k_new, v_new, out and ws", {q, k_new, v_new, out, ws})) != RESA_OK) return st;
   if (f < 1 || f > resa::kMaxRectF) return fail(RESA_ERR_UNSUPPORTED, "f %d outside 1 .. %d", f, resa::kMaxRectF);
   if (f > v.max_seq_len) return fail(RESA_ERR_INVALID, "f %d exceeds max_seq_len %d", f, v.max_seq_len);
   if (!(scale > 0.f) || !isfinite(scale)) return fail(RESA_ERR_INVALID, "scale must be positive and finite");

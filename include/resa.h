@@ -15,6 +15,10 @@
  *    included; the library never allocates or frees device memory.
  *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the default
  *    stream) and never synchronises with the host.
+ *  - Alignment: the cache's k_pages, v_pages and desc, and every q, k_new,
+ *    v_new, out and workspace pointer, must be 16-byte aligned; block_table,
+ *    seq_lens, idx and count 4-byte aligned (allocations from hipMalloc, and
+ *    their rows, are). A misaligned pointer returns RESA_ERR_INVALID.
  *  - Arguments are validated on the host before any launch. A bad argument
  *    returns RESA_ERR_INVALID or RESA_ERR_UNSUPPORTED and launches nothing; a
  *    failed launch returns RESA_ERR_HIP. resa_last_error() then gives a message.

@@ -151,6 +151,33 @@ def test_update_descriptor_argument_checks(lib):
     assert lib.resa_update_descriptors(ctypes.byref(c), None, None, -1, None) == R.RESA_ERR_INVALID
 
 
+def test_misaligned_pointers_are_rejected(lib):
+    """Element arrays must be 16-byte aligned, integer arrays 4-byte aligned;
+    the check runs on the host, so the fake addresses are never touched."""
+    for bad in (dict(k_pages=0x1002), dict(v_pages=0x2008), dict(desc=0x3004), dict(block_table=0x4002),
+                dict(seq_lens=0x5001)):
+        assert lib.resa_update_descriptors(ctypes.byref(_cache(**bad)), None, None, 0, None) == R.RESA_ERR_INVALID
+    c = _cache()
+    ok, odd = ctypes.c_void_p(0xC000), ctypes.c_void_p(0xC008)
+    assert lib.resa_update_descriptors(ctypes.byref(c), odd, ok, 1, None) == R.RESA_ERR_INVALID
+    assert lib.resa_update_descriptors(ctypes.byref(c), ok, odd, 1, None) == R.RESA_ERR_INVALID
+    p = R.ResaSelectParams(16, 1, 0.1)
+    need = lib.resa_select_workspace_size(ctypes.byref(c))
+    assert lib.resa_select_blocks(ctypes.byref(c), odd, ctypes.byref(p), ok, ok, 16, ok, need,
+                                  None) == R.RESA_ERR_INVALID
+    assert lib.resa_select_blocks(ctypes.byref(c), ok, ctypes.byref(p), ctypes.c_void_p(0xC002), ok, 16, ok, need,
+                                  None) == R.RESA_ERR_INVALID
+    assert lib.resa_append_select(ctypes.byref(c), odd, odd, ok, ctypes.byref(p), ok, ok, 16, ok, need,
+                                  None) == R.RESA_ERR_INVALID
+    need = lib.resa_decode_workspace_size(ctypes.byref(c), 16)
+    assert lib.resa_sparse_decode(ctypes.byref(c), ok, ok, ok, 16, ctypes.c_float(0.1), odd, ok, need,
+                                  None) == R.RESA_ERR_INVALID
+    need = lib.resa_rectify_workspace_size(ctypes.byref(c), 32)
+    assert lib.resa_rectify(ctypes.byref(c), ok, ok, ok, 32, ctypes.c_float(0.1), ok, odd, need,
+                            None) == R.RESA_ERR_INVALID
+    assert "aligned" in lib.resa_last_error().decode()
+
+
 def test_cache_subset_offsets_pointers():
     """A sub-batch view keeps the pages and offsets the block-table and length
     pointers to its first sequence (no device memory is touched)."""
