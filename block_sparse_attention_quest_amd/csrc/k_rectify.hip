@@ -95,10 +95,17 @@ __device__ long long block_exclusive_scan(long long v, long long* sh, long long*
 // contiguous runs of sequences, then of segments; consecutive boundaries are
 // stepped without division (lo(w) = w q + floor(w r / P), TT = q P + r).
 // NT threads of one workgroup build the plan.
-template <int NT>
+// IN_LDS (batches up to kPlanLdsSeqs): lengths and tile prefixes stay in LDS,
+// so the segment passes make no further global round trip; otherwise they are
+// read back from the workspace and seq_lens.
+constexpr int kPlanLdsSeqs = 1024;
+
+template <int NT, bool IN_LDS>
 __device__ __forceinline__ void rect_plan(const RectArgs& a) {
   const CacheView& c = a.c;
   __shared__ long long sh[NT / 64];
+  __shared__ int s_len[IN_LDS ? kPlanLdsSeqs : 1];
+  __shared__ long long s_pt[IN_LDS ? kPlanLdsSeqs : 1];
   const int tid = threadIdx.x;
   const long long Hkv = c.Hkv;
   const int RT = a.rtiles;
@@ -108,28 +115,43 @@ __device__ __forceinline__ void rect_plan(const RectArgs& a) {
     return max(1, L - a.f + r_last / c.G + 1);
   };
   auto rt_tiles = [&](int L, int rt) { return (long long)(key_end(L, rt) + kRectTileKeys - 1) / kRectTileKeys; };
-  auto tiles = [&](int b) {  // all row tiles of one (sequence, KV head)
+  auto tiles_of = [&](int L) {  // all row tiles of one (sequence, KV head)
     long long t = 0;
-    for (int rt = 0; rt < RT; ++rt) t += rt_tiles(c.seq_lens[b], rt);
+    for (int rt = 0; rt < RT; ++rt) t += rt_tiles(L, rt);
     return t;
   };
 
   const int per_b = (c.B + NT - 1) / NT;
   const int b0 = min(c.B, tid * per_b), b1 = min(c.B, b0 + per_b);
   long long tloc = 0;
-  for (int b = b0; b < b1; ++b) tloc += tiles(b);
+  for (int b = b0; b < b1; ++b) {
+    const int L = c.seq_lens[b];
+    if (IN_LDS) s_len[b] = L;
+    tloc += tiles_of(L);
+  }
   long long tsum;
   long long pt = block_exclusive_scan<NT>(tloc, sh, &tsum);
   for (int b = b0; b < b1; ++b) {
-    a.ptile[b] = pt;
-    pt += tiles(b);
+    if (IN_LDS)
+      s_pt[b] = pt;
+    else
+      a.ptile[b] = pt;
+    pt += tiles_of(IN_LDS ? s_len[b] : c.seq_lens[b]);
   }
+  auto len_of = [&](int b) {
+    if constexpr (IN_LDS) return s_len[b];
+    else return c.seq_lens[b];
+  };
+  auto ptile_of = [&](int b) {
+    if constexpr (IN_LDS) return s_pt[b];
+    else return a.ptile[b];
+  };
   const long long TT = tsum * Hkv;
   // whole rounds of `target` workgroups, as few as keep ranges <= kMaxItemTiles
   long long P = a.target * ceil_div_ll(TT, (long long)a.target * kMaxItemTiles);
   if (P > TT) P = TT;
   const long long q = TT / P, r = TT % P;
-  __syncthreads();  // ptile visible to the workgroup
+  __syncthreads();  // lengths and prefixes visible to the workgroup
 
   const int S = c.B * c.Hkv * RT;
   const int per_s = (S + NT - 1) / NT;
@@ -137,10 +159,10 @@ __device__ __forceinline__ void rect_plan(const RectArgs& a) {
   // segment s: first tile, end tile, and the range starts strictly inside
   auto segment = [&](int s, long long& as, long long& es, long long& wl, long long& wh) {
     const int b = s / (c.Hkv * RT), g = (s / RT) % c.Hkv, rt = s % RT;
-    const int L = c.seq_lens[b];
+    const int L = len_of(b);
     long long before = 0;  // key tiles of the sequence's earlier row tiles
     for (int x = 0; x < rt; ++x) before += rt_tiles(L, x);
-    as = a.ptile[b] * Hkv + g * tiles(b) + before;
+    as = ptile_of(b) * Hkv + g * tiles_of(L) + before;
     es = as + rt_tiles(L, rt);
     wl = ceil_div_ll((as + 1) * P, TT);
     wh = ceil_div_ll(es * P, TT) - 1;
@@ -157,7 +179,7 @@ __device__ __forceinline__ void rect_plan(const RectArgs& a) {
     long long as, es, wl, wh;
     segment(s, as, es, wl, wh);
     const int b = s / (c.Hkv * RT), g = (s / RT) % c.Hkv, rt = s % RT;
-    const int kend = key_end(c.seq_lens[b], rt);
+    const int kend = key_end(len_of(b), rt);
     const int cnt = 1 + int(wh >= wl ? wh - wl + 1 : 0);
     a.groups[s] = make_int2(int(fi), cnt);
     // the range that holds tile as starts exactly there: this item is its first
@@ -193,7 +215,12 @@ template <typename T, int D>
 __global__ __launch_bounds__(64) void k_rect_prep(RectArgs a, const void* __restrict__ k_new,
                                                   const void* __restrict__ v_new) {
   if (blockIdx.x == gridDim.x - 1) {
-    if (blockIdx.y == 0 && blockIdx.z == 0) rect_plan<64>(a);
+    if (blockIdx.y == 0 && blockIdx.z == 0) {
+      if (a.c.B <= kPlanLdsSeqs)
+        rect_plan<64, true>(a);
+      else
+        rect_plan<64, false>(a);
+    }
     return;
   }
   const CacheView& c = a.c;

@@ -219,6 +219,26 @@ def test_rectify_mixed_lengths_small(f):
     P.assert_desc_equal(r.cache.desc, oc)
 
 
+def test_rectify_batch_beyond_the_plan_lds():
+    """1100 short sequences (more than the 1024 whose lengths and tile prefixes
+    the work plan keeps in LDS): the plan reads them back from global memory."""
+    w = W.rectify_mixed(batch=1100, len_range=(17, 90), seed=23, f=4).replace(num_q_heads=8, num_kv_heads=2)
+    print(f"[case] rectify of {w.batch} sequences f={w.f} lens {min(w.prefill_lens)}..{max(w.prefill_lens)}",
+          flush=True)
+    r = _runner(w)
+    oc = P.oracle_cache(w)
+    got = r.rectify_only()
+    q, k, v = r.rect_inputs[-1]
+    for b in range(w.batch):
+        oc.seq_lens[b] += w.f
+    ref = O.rectify(oc, P.f64(q), P.f64(k), P.f64(v), 1.0 / math.sqrt(w.head_dim))
+    torch.cuda.synchronize()
+    err = P.out_error(P.f64(got), ref, "bf16")
+    print(f"[result] rectify of {w.batch} sequences: error beyond output rounding {err:.3g}")
+    assert err <= P.ATOL["bf16"]
+    P.assert_desc_equal(r.cache.desc, oc)
+
+
 def test_rectify_of_some_sequences_then_decode():
     """Continuous batching: sequences 1 .. 2 of 3 are rectified through a
     sub-batch view of the cache while sequence 0 is not; decoding of all three
