@@ -396,13 +396,15 @@ struct MfmaBlock {
   }
 };
 
-// grid: x = split, y = KV head, z = sequence; 256 threads.
+// grid: x = split, y = KV head, z = sequence (dealt to XCDs by xcd_pair_remap);
+// 256 threads.
 template <int D, int G, int NB>
 __global__ __launch_bounds__(kDecThreads) void k_decode_mfma(DecodeArgs a) {
   constexpr int KS = D / 32, DT = D / 16;
   __shared__ DecMerge<G, D> sm;
   const CacheView& c = a.c;
-  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int3 w = xcd_pair_remap(blockIdx.x, blockIdx.y, blockIdx.z, a.splits, c.Hkv);
+  const int s = w.x, g = w.y, b = w.z;  // split, KV head, sequence
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane & 15, j = lane >> 4;  // head column, token group
   const size_t gi = size_t(b) * c.Hkv + g;

@@ -18,6 +18,22 @@ constexpr int kMaxRectF = 1024;
 constexpr size_t kLastLevelCacheBytes = size_t(256) << 20;  // MI355X Infinity Cache
 constexpr int kCachePolicyNT = 2;  // cache-policy operand of the direct-to-LDS load: non-temporal
 
+// Workgroups are dealt to the 8 XCDs (each with its own L2) in turn by linear
+// id. With a grid of NX workgroups per (sequence, KV head) pair, laid out
+// (x, KV head, sequence), this remap runs every workgroup of pair gi on XCD
+// gi % 8. Kernels launched over a (KV head, sequence, ...) grid run pair gi
+// there too (the top-n before the decode, the merge after it), so what one
+// writes the next finds in that XCD's L2. Applied when the KV heads are a
+// multiple of 8: every XCD then holds one-eighth of the heads of every
+// sequence, whatever the length mix. Returns the (x, KV head, sequence) the
+// workgroup takes.
+__device__ __forceinline__ int3 xcd_pair_remap(int x, int g, int b, int NX, int Hkv) {
+  if ((Hkv & 7) != 0) return make_int3(x, g, b);
+  const int i = x + NX * (g + Hkv * b);
+  const int k = i >> 3, gi = (i & 7) + 8 * (k / NX);
+  return make_int3(k % NX, gi % Hkv, gi / Hkv);
+}
+
 // Row stride (in keys) of the selection workspace: max_blocks_per_seq rounded
 // up to even, so every row starts on 16 bytes.
 __host__ __device__ constexpr int key_stride(int maxb) { return (maxb + 1) & ~1; }
