@@ -81,10 +81,13 @@ def decode_traffic(w):
     workload or on a different version of the decode kernels."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "traffic_decode_gqa128k_b4.json")
-    src = os.path.join(ROOT, "block_sparse_attention_quest_amd", "csrc", "k_decode.hip")
+    csrc = os.path.join(ROOT, "block_sparse_attention_quest_amd", "csrc")
     try:
         rec = json.load(open(path))
-        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        h = hashlib.sha256()
+        for name in ("k_decode.hip", "resa_internal.h"):  # the decode kernels and their helpers
+            h.update(open(os.path.join(csrc, name), "rb").read())
+        digest = h.hexdigest()
     except (OSError, ValueError):
         return None
     if rec.get("source_sha256") != digest or rec.get("workload") != w.name:
