@@ -407,3 +407,128 @@ def test_loop_without_rectification_keeps_sparse_phase_kv():
     for t in range(8):
         pos = 40 + t
         assert np.array_equal(cache.k[cache.block_table[0, pos // 16], 0, pos % 16], ks[t, 0, 0])
+
+
+# --- per-group wiring of the batched calls ------------------------------------
+
+def _brute_desc(K):
+    """Per-block channel min/max of K [L][d] by explicit loops."""
+    L, d = K.shape
+    out = []
+    for j in range(-(-L // 16)):
+        lo, hi = [math.inf] * d, [-math.inf] * d
+        for t in range(j * 16, min(L, j * 16 + 16)):
+            for c in range(d):
+                x = float(K[t, c])
+                lo[c] = min(lo[c], x)
+                hi[c] = max(hi[c], x)
+        out.append((lo, hi))
+    return out
+
+
+def test_batched_select_pools_each_group_over_its_own_heads_and_kv_head():
+    """'What carries the argument': each GQA group pools its own G query heads
+    and scores its own KV head's descriptors. Every (sequence, group) gets its
+    own planted blocks, along that group's pooled query, so a slice of the
+    wrong heads or the wrong KV head's descriptors picks other blocks."""
+    rng = np.random.default_rng(21)
+    B, Hkv, G, d = 2, 3, 2, 8
+    Hq = Hkv * G
+    lens = [150, 237]
+    cache = _random_cache(rng, B, Hkv, d, lens)
+    q = rng.standard_normal((B, Hq, d))
+    n_min, r, n_local = 3, 0.1, 1
+    planted = {}
+    for b, L in enumerate(lens):
+        M = O.num_blocks(L)
+        perm = rng.permutation(M - 1)  # disjoint planted blocks per group
+        for g in range(Hkv):
+            qbar = q[b, g * G:(g + 1) * G].mean(axis=0)
+            u = qbar / np.linalg.norm(qbar)
+            blocks = sorted(perm[2 * g:2 * g + 2].tolist())
+            planted[b, g] = blocks
+            for j in blocks:
+                cache.k[cache.block_table[b, j], g, :] += 12.0 * u
+    cache.rebuild()
+    idx, counts, scores = O.select(cache, q, n_min, r, n_local)
+    distinct = set()
+    for b, L in enumerate(lens):
+        M = O.num_blocks(L)
+        n = O.active_block_count(M, n_min, r)
+        assert counts[b] == n == 3
+        for g in range(Hkv):
+            # brute force: the group's own heads, its own KV head's raw keys
+            qbar = [sum(float(q[b, h, c]) for h in range(g * G, (g + 1) * G)) / G for c in range(d)]
+            desc = _brute_desc(cache.seq(b, g, "k"))
+            s = [sum(max(qbar[c] * lo[c], qbar[c] * hi[c]) for c in range(d)) for lo, hi in desc]
+            np.testing.assert_allclose(scores[b][g], s, rtol=1e-13, atol=1e-13)
+            ref = _rank_selection(np.array(s), n, n_local)
+            assert idx[b][g].tolist() == ref, (b, g)
+            # the planted blocks of this group, plus its newest block
+            assert ref == sorted(planted[b, g] + [M - 1]), (b, g, ref, planted[b, g])
+            distinct.add(tuple(ref))
+    assert len(distinct) == B * Hkv  # every group's set is its own
+
+
+def test_dense_decode_equals_sdpa_with_gqa_head_map():
+    """The dense-decoding baseline the sparse path is compared with (Fig. 6
+    caption): query head h attends to every cached token of KV head h // G."""
+    rng = np.random.default_rng(22)
+    B, Hkv, G, d = 2, 2, 3, 8
+    Hq = Hkv * G
+    lens = [41, 70]
+    cache = _random_cache(rng, B, Hkv, d, lens)
+    q = rng.standard_normal((B, Hq, d))
+    scale = 0.37
+    out = O.dense_decode(cache, q, scale)
+    for b in range(B):
+        k = torch.from_numpy(np.stack([cache.seq(b, g, "k") for g in range(Hkv)]))
+        v = torch.from_numpy(np.stack([cache.seq(b, g, "v") for g in range(Hkv)]))
+        k = k.repeat_interleave(G, dim=0).numpy()   # head h reads KV head h // G
+        v = v.repeat_interleave(G, dim=0).numpy()
+        ref = _sdpa(q[b][:, None, :] * (scale * math.sqrt(d)), k, v)[:, 0]
+        np.testing.assert_allclose(out[b], ref, rtol=1e-12, atol=1e-12)
+        # and it is the sparse decode with every block selected
+        M = O.num_blocks(lens[b])
+        for g in range(Hkv):
+            sp = O.sparse_decode_group(q[b, g * G:(g + 1) * G], cache.seq(b, g, "k"), cache.seq(b, g, "v"),
+                                       range(M), scale)
+            np.testing.assert_allclose(out[b, g * G:(g + 1) * G], sp, rtol=1e-12, atol=1e-12)
+
+
+def test_loop_rectifies_after_every_f_th_step_exactly():
+    """'Every f decoding steps' ('What carries the argument', Fig. 2): the
+    rectification follows decode steps f-1, 2f-1, ... (0-based), after that
+    step's decode, and covers the f tokens those steps appended."""
+    rng = np.random.default_rng(23)
+    B, Hq, Hkv, d, steps, f = 1, 4, 1, 8, 14, 4
+    L0 = 37
+    cache = _random_cache(rng, B, Hkv, d, [L0], extra_blocks=3)
+    qs = rng.standard_normal((steps, B, Hq, d))
+    ks = rng.standard_normal((steps, B, Hkv, d))
+    vs = rng.standard_normal((steps, B, Hkv, d))
+    log = []
+
+    def rect_inputs(t):
+        log.append(("rectify", t, cache.seq_lens[0]))
+        return (rng.standard_normal((B, f, Hq, d)), np.full((B, f, Hkv, d), 100.0 + t),
+                np.full((B, f, Hkv, d), -100.0 - t))
+
+    def on_step(t, c, o, idx):
+        log.append(("step", t, c.seq_lens[0]))
+
+    O.resa_loop(cache, steps, f, n_min=2, r=0.25, n_local=1, scale=0.35,
+                step_inputs=lambda t: (qs[t], ks[t], vs[t]), rectify_inputs=rect_inputs, on_step=on_step)
+    expect = []
+    for t in range(steps):
+        expect.append(("step", t, L0 + t + 1))
+        if t % f == f - 1:
+            expect.append(("rectify", t, L0 + t + 1))
+    assert log == expect
+    # the rectified rows overwrote exactly the f tokens appended since the last one
+    for t in (f - 1, 2 * f - 1, 3 * f - 1):
+        for pos in range(L0 + t + 1 - f, L0 + t + 1):
+            assert np.all(cache.k[cache.block_table[0, pos // 16], 0, pos % 16] == 100.0 + t)
+    for t in range(3 * f, steps):  # appended after the last rectification: untouched
+        pos = L0 + t
+        assert np.array_equal(cache.k[cache.block_table[0, pos // 16], 0, pos % 16], ks[t, 0, 0])
