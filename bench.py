@@ -109,11 +109,12 @@ def cpu_baseline(w, first_step, budget_s):
     from block_sparse_attention_quest_amd import workloads as W
     from oracle import resa_oracle as O
 
+    cores = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        cores = 1
+        blas_threads = 1
     G, d = w.group, w.head_dim
     scale = 1.0 / math.sqrt(d)
     groups = [(b, g) for b in range(w.batch) for g in range(w.num_kv_heads)]
@@ -161,10 +162,13 @@ def cpu_baseline(w, first_step, budget_s):
     # per step: every group decodes once; every f steps B * f * Hq rows are rectified
     sec_per_step = w.batch * w.num_kv_heads * dec + (w.batch * w.num_q_heads * row if w.f > 0 else 0.0)
     return {"value": 1.0 / sec_per_step, "unit": "steps/s", "cores": int(cores), "kind": "oracle",
+            "blas_threads": int(blas_threads),
             "sample": (f"{len(t_dec)} of {w.batch * w.num_kv_heads} (sequence, KV-head) groups of one decode step "
                        f"and {len(t_row)} rectified query rows over the full context, timed on the host in float64 "
                        f"NumPy and scaled to the whole batch ({dec * 1e3:.1f} ms per group step, "
-                       f"{row * 1e3:.1f} ms per rectified row)")}
+                       f"{row * 1e3:.1f} ms per rectified row); cores = the host threads this process may run on, "
+                       f"of which the matrix products use {blas_threads} BLAS threads and the element-wise "
+                       f"NumPy steps one")}
 
 
 # ---------------------------------------------------------------------------
@@ -382,6 +386,12 @@ def main():
         return prefill_only(base, args)
     if base.steps == 0:
         return rectify_only(base, args)
+    # The timed window holds whole rectification periods: any f consecutive
+    # steps contain exactly one rectification, so the rate is amortised over
+    # it whatever K is asked for (K is rounded up to a multiple of f).
+    K_req = K
+    if base.f > 0:
+        K = -(-K // base.f) * base.f
     w = base.replace(steps=Wu + K + MEASURE_STEPS)
     t_setup = time.perf_counter()
     print(f"[bench] setting up {w.name}: batch {w.batch}, prefill {w.prefill_lens[0]}, steps {w.steps}",
@@ -552,6 +562,17 @@ def main():
     rkv, rflops = rectify_work(w, L_list, w.f) if w.f > 0 else (0, 0)
     full_cache = sum(w.num_kv_heads * L * 2 * w.head_dim * (2 if w.dtype == "bf16" else 4) for L in L_list)
     step_alg = sb["append"] + sb["select"] + sb["decode"] + (rkv / w.f if w.f > 0 else 0)
+    # the bytes the timed window actually moved: every timed step's sparse work
+    # at its own lengths, plus the rectifications that ran inside the window
+    win_bytes = 0
+    n_rect_win = 0
+    for t in range(Wu, Wu + K):
+        Lt = [L + t + 1 for L in w.prefill_lens]
+        sbt = step_bytes(w, Lt, [n_for(-(-L // 16), w) for L in Lt])
+        win_bytes += sbt["append"] + sbt["select"] + sbt["decode"]
+        if t in rect_in:
+            n_rect_win += 1
+            win_bytes += rectify_work(w, Lt, w.f)[0]
     dec_gbs = sb["decode"] / (dec_ms * 1e-3) / 1e9
     sel_gbs = (sb["append"] + sb["select"]) / (sel_ms * 1e-3) / 1e9
     rect_us = stage_us["rectify"]
@@ -579,7 +600,12 @@ def main():
                      "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": decode_traffic(w),
                      "alg_bytes_per_launch": sb["decode"], "avg_launch_us": round(dec_ms * 1e3, 2)},
-        "hbm_gbs_step": round(step_alg / (ms_per_step * 1e-3) / 1e9, 1),
+        "steps_requested": K_req,
+        "value_basis": (f"{K} timed steps = {K // w.f} whole rectification period(s) of f = {w.f}, "
+                        f"{n_rect_win} rectification(s) inside the window" if w.f > 0 else
+                        f"{K} timed steps, no rectification (f = 0)"),
+        "hbm_gbs_step": round(win_bytes / (total_ms * 1e-3) / 1e9, 1),
+        "alg_bytes_window": int(win_bytes),
         "alg_bytes_per_step": int(step_alg),
         "eq6_fraction": round(step_alg / full_cache, 5),
         "selected_kv_bytes_per_group": sb["selected_kv"] / (w.batch * w.num_kv_heads),
