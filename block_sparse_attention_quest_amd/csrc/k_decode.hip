@@ -363,14 +363,19 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
 // 16x16x32 (A: the K tile, lane l holding token l % 16 and channels
 // 32 ks + 8 (l / 16) + [0, 8); B: the group's queries in the same channel order,
 // lane l holding head l % 16, zero for l % 16 >= G). The result leaves lane l
-// with head l % 16 and tokens 4 (l / 16) + [0, 4), which is exactly where the
-// B operand of a 16x16x16 MFMA wants P^T, so after the online softmax the
-// probabilities (rounded to bf16; the denominator sums the same rounded values)
-// go straight into O^T += V^T P^T, D/16 MFMAs whose A operands are 8-byte
-// pieces of the channel-major V tile (lane l: channel 16 dt + l % 16, tokens
-// 4 (l / 16) + [0, 4)). A lane keeps the running max, denominator and O^T
-// column of one head: no cross-lane sums, one max over the four lane groups
-// per block.
+// with head l % 16 and tokens 4 (l / 16) + [0, 4), so after the online
+// softmax the probabilities go straight into O^T += V^T P^T with no data
+// movement: D/16 MFMAs 16x16x32 whose A operands are the lane's 8-byte piece
+// of the channel-major V tile (lane l: channel 16 dt + l % 16, tokens
+// 4 (l / 16) + [0, 4)) written twice, and whose B operand is that lane's
+// probabilities as the bf16 pair hi + lo (hi = bf16(p), lo = bf16(p - hi)):
+// k = 8 (l / 16) + [0, 4) takes hi, k = 8 (l / 16) + [4, 8) lo, so one
+// instruction adds V^T P_hi^T + V^T P_lo^T, and p carries about 16
+// significant bits instead of 8 (a row whose weight sits on a few keys would
+// otherwise carry up to 2^-9 of p's rounding times the spread of its values).
+// The denominator sums the same hi + lo values. A lane keeps the running max,
+// denominator and O^T column of one head: no cross-lane sums, one max over the
+// four lane groups per block.
 template <int I, int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
   if constexpr (I < N) {
@@ -491,17 +496,34 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_mfma(DecodeArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       p[r] = sc[r] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(fmaf(sc[r], a.scale_log2, -m));
+    // p as the bf16 pair hi + lo (hi = bf16(p), lo = bf16(p - hi): about 16
+    // significant bits), so a row whose weight sits on a few keys keeps its
+    // accuracy; the denominator sums the same hi + lo values
     const f32x2_t p01 = {p[0], p[1]}, p23 = {p[2], p[3]};
     const uint32_t w01 = __builtin_bit_cast(uint32_t, __builtin_convertvector(p01, bf16x2_t));
     const uint32_t w23 = __builtin_bit_cast(uint32_t, __builtin_convertvector(p23, bf16x2_t));
+    const f32x2_t l01 = {p[0] - bf16_lo(w01), p[1] - bf16_hi(w01)}, l23 = {p[2] - bf16_lo(w23), p[3] - bf16_hi(w23)};
+    const uint32_t x01 = __builtin_bit_cast(uint32_t, __builtin_convertvector(l01, bf16x2_t));
+    const uint32_t x23 = __builtin_bit_cast(uint32_t, __builtin_convertvector(l23, bf16x2_t));
     lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w01), __builtin_bit_cast(bf16x2_t, ones), lsum,
                                            false);
     lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w23), __builtin_bit_cast(bf16x2_t, ones), lsum,
                                            false);
-    const s16x4_t pb = __builtin_bit_cast(s16x4_t, make_uint2(w01, w23));
+    lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x01), __builtin_bit_cast(bf16x2_t, ones), lsum,
+                                           false);
+    lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x23), __builtin_bit_cast(bf16x2_t, ones), lsum,
+                                           false);
+    // One 16x16x32 MFMA per channel tile takes both halves: lane (h, j)
+    // supplies k = 8 j + [0, 8) as (hi of tokens 4 j .. 4 j + 3, lo of the same
+    // tokens) in B, and the A operand repeats its V piece of those four tokens,
+    // so O^T += V^T P_hi^T + V^T P_lo^T in one instruction.
+    const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, make_uint4(w01, w23, x01, x23));
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, cur.v[dt]), pb, o[dt], 0, 0, 0);
+    for (int dt = 0; dt < DT; ++dt) {
+      const uint2 vp = cur.v[dt];
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, make_uint4(vp.x, vp.y, vp.x, vp.y)),
+                                                      pb, o[dt], 0, 0, 0);
+    }
   };
 
   for (int it0 = 0; it0 < nw; it0 += NB) {

@@ -98,6 +98,12 @@ SMALL = [
     ("fp32_g8_d64", "fp32", 1, 16, 2, 64, (900,), 5, 5, 8, 0.1, 1),
     ("fp32_g2_d128", "fp32", 2, 4, 2, 128, (150, 420), 6, 3, 4, 0.2, 2),
     ("fp32_g1_d64", "fp32", 2, 2, 2, 64, (64, 257), 4, 4, 2, 0.25, 0),
+    # the remaining (dtype, group, head_dim) instantiations of the decode
+    ("bf16_g2_d64", "bf16", 2, 4, 2, 64, (410, 95), 5, 5, 4, 0.1, 1),
+    ("fp32_g1_d128", "fp32", 2, 2, 2, 128, (180, 333), 4, 4, 4, 0.1, 1),
+    ("fp32_g2_d64", "fp32", 2, 4, 2, 64, (600, 77), 4, 4, 4, 0.1, 1),
+    ("fp32_g4_d64", "fp32", 2, 8, 2, 64, (260, 1030), 5, 5, 4, 0.1, 1),
+    ("fp32_g8_d128", "fp32", 1, 16, 2, 128, (700,), 4, 4, 8, 0.1, 1),
 ]
 
 

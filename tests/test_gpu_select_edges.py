@@ -147,3 +147,12 @@ def test_select_short_rows(kind):
 def test_select_long_rows(kind, lens):
     q1 = 0.0 if kind == "integer_ties" else TINY
     _run(kind, lens, (16, 0.1, 1), 1.0, q1, Hkv=1, seed=11)
+
+
+@pytest.mark.parametrize("keys_per_thread", [8, 10, 12, 14, 16, 20, 24])
+def test_select_every_register_count(keys_per_thread):
+    """Rows of 8 to 24 keys per thread (about 128K to 384K tokens): each of the
+    selection's register-count builds, on a ranked threshold group."""
+    M = keys_per_thread * 1000  # ceil(M / 1024) == keys_per_thread
+    assert -(-M // 1024) == keys_per_thread
+    _run("ranked_group", [M * 16 - 9, 7000], (16, 0.1, 1), 1.0, TINY, Hkv=1, seed=keys_per_thread)
