@@ -5,7 +5,9 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
 #include <initializer_list>
+#include <mutex>
 
 #include "resa_internal.h"
 
@@ -88,6 +90,35 @@ resa_status check_params(const resa_select_params* p) {
   if (p->n_min < 1) return fail(RESA_ERR_INVALID, "n_min must be >= 1");
   if (p->n_local < 0) return fail(RESA_ERR_INVALID, "n_local must be >= 0");
   if (!(p->r > 0.0 && p->r <= 1.0)) return fail(RESA_ERR_INVALID, "r must be in (0, 1]");
+  return RESA_OK;
+}
+
+// Scratch of resa_sparse_decode_noalloc: the decode's split partials live in
+// this array instead of a caller workspace. Each GPU the library runs on holds
+// its own copy until the process ends; host code never uses the array's name as
+// an address, only the device pointer hipGetSymbolAddress returns for it.
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The scratch array's address on `dev` (the current device), looked up once
+// per device.
+resa_status scratch_on_device(int dev, void** out) {
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+      if (!p) return fail(RESA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
   return RESA_OK;
 }
 
@@ -193,6 +224,37 @@ resa_status resa_sparse_decode(const resa_cache* cache, const void* q, const int
   if (!ws || ws_bytes < need) return fail(RESA_ERR_WORKSPACE, "decode workspace %zu < %zu bytes", ws_bytes, need);
   return hip_status(resa::launch_decode(v, q, idx, count, n_cap, scale, out, ws, static_cast<hipStream_t>(stream)),
                     "resa_sparse_decode");
+}
+
+resa_status resa_sparse_decode_noalloc(const resa_cache* cache, const void* q, const int32_t* idx,
+                                       const int32_t* count, int32_t n_cap, float scale, void* out,
+                                       void* stream) {
+  resa::CacheView v;
+  resa_status st = check_cache(cache, &v);
+  if (st != RESA_OK) return st;
+  if (!q || !idx || !count || !out) return fail(RESA_ERR_INVALID, "q, idx, count and out must not be NULL");
+  if ((st = check_aligned16("q and out", {q, out})) != RESA_OK) return st;
+  if (!aligned(idx, 4) || !aligned(count, 4)) return fail(RESA_ERR_INVALID, "idx and count must be 4-byte aligned");
+  if (n_cap < 1 || n_cap > v.maxb) return fail(RESA_ERR_INVALID, "n_cap %d outside 1 .. max_blocks_per_seq", n_cap);
+  if (!(scale > 0.f) || !isfinite(scale)) return fail(RESA_ERR_INVALID, "scale must be positive and finite");
+  const size_t need = resa::decode_ws_bytes(v, n_cap);
+  if (need > kNoAllocScratchBytes)
+    return fail(RESA_ERR_UNSUPPORTED, "the decode needs %zu bytes of scratch; resa_sparse_decode_noalloc holds %zu",
+                need, kNoAllocScratchBytes);
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(RESA_ERR_UNSUPPORTED, "device %d (at most %d devices)", dev, kMaxDevices);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (s) {
+    hipDevice_t sdev = -1;
+    if ((e = hipStreamGetDevice(s, &sdev)) != hipSuccess) return hip_status(e, "hipStreamGetDevice");
+    if (sdev != dev)
+      return fail(RESA_ERR_INVALID, "stream belongs to device %d but device %d is current", int(sdev), dev);
+  }
+  void* ws = nullptr;
+  if ((st = scratch_on_device(dev, &ws)) != RESA_OK) return st;
+  return hip_status(resa::launch_decode(v, q, idx, count, n_cap, scale, out, ws, s), "resa_sparse_decode_noalloc");
 }
 
 resa_status resa_rectify(const resa_cache* cache, const void* q, const void* k_new, const void* v_new,

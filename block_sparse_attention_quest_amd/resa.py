@@ -22,7 +22,8 @@ _STATUS = {0: "RESA_OK", 1: "RESA_ERR_INVALID", 2: "RESA_ERR_UNSUPPORTED",
            3: "RESA_ERR_WORKSPACE", 4: "RESA_ERR_HIP"}
 EXPORTED = ("resa_n_cap", "resa_select_workspace_size", "resa_decode_workspace_size",
             "resa_rectify_workspace_size", "resa_update_descriptors", "resa_select_blocks",
-            "resa_append_select", "resa_sparse_decode", "resa_rectify", "resa_last_error")
+            "resa_append_select", "resa_sparse_decode", "resa_sparse_decode_noalloc", "resa_rectify",
+            "resa_last_error")
 
 
 class ResaError(RuntimeError):
@@ -71,6 +72,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.resa_append_select.restype = i32
     lib.resa_sparse_decode.argtypes = [cp, vp, vp, vp, i32, ctypes.c_float, vp, vp, sz, vp]
     lib.resa_sparse_decode.restype = i32
+    lib.resa_sparse_decode_noalloc.argtypes = [cp, vp, vp, vp, i32, ctypes.c_float, vp, vp]
+    lib.resa_sparse_decode_noalloc.restype = i32
     lib.resa_rectify.argtypes = [cp, vp, vp, vp, i32, ctypes.c_float, vp, vp, sz, vp]
     lib.resa_rectify.restype = i32
     lib.resa_last_error.argtypes, lib.resa_last_error.restype = [], ctypes.c_char_p
@@ -198,6 +201,13 @@ def resa_sparse_decode(cache: PagedKVCache, q: torch.Tensor, idx: torch.Tensor, 
     _check(load().resa_sparse_decode(ctypes.byref(cache.struct), _ptr(q), _ptr(idx), _ptr(count), int(n_cap),
                                      ctypes.c_float(scale), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
                                      _stream(stream)))
+
+
+def resa_sparse_decode_noalloc(cache: PagedKVCache, q: torch.Tensor, idx: torch.Tensor, count: torch.Tensor,
+                               n_cap: int, out: torch.Tensor, scale: Optional[float] = None, stream=None) -> None:
+    scale = 1.0 / math.sqrt(cache.head_dim) if scale is None else scale
+    _check(load().resa_sparse_decode_noalloc(ctypes.byref(cache.struct), _ptr(q), _ptr(idx), _ptr(count), int(n_cap),
+                                             ctypes.c_float(scale), _ptr(out), _stream(stream)))
 
 
 def resa_rectify(cache: PagedKVCache, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, f: int,

@@ -12,7 +12,9 @@
  * Conventions (all entry points):
  *  - Pointers are device pointers unless marked (host). Arrays are row-major with
  *    the head dimension innermost. The caller owns every buffer, the workspace
- *    included; the library never allocates or frees device memory.
+ *    included; the library never allocates or frees device memory (the one
+ *    exception, resa_sparse_decode_noalloc's scratch array, is a static device
+ *    array loaded with the library, not an allocation).
  *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the default
  *    stream) and never synchronises with the host.
  *  - Alignment: the cache's k_pages, v_pages and desc, and every q, k_new,
@@ -31,9 +33,10 @@
  *    matter and are dead on return, so one workspace may serve all calls issued
  *    in order on one stream. Calls that may run concurrently need separate
  *    workspaces.
- *  - The library holds no mutable state apart from the thread-local error text,
- *    so calls on different streams from different host threads are safe as long
- *    as they do not share output buffers or workspace.
+ *  - The library holds no mutable state apart from the thread-local error text
+ *    (and resa_sparse_decode_noalloc's scratch array), so calls on different
+ *    streams from different host threads are safe as long as they do not share
+ *    output buffers or workspace.
  */
 #ifndef RESA_H
 #define RESA_H
@@ -185,6 +188,29 @@ resa_status resa_append_select(const resa_cache* cache, const void* k_new, const
 resa_status resa_sparse_decode(const resa_cache* cache, const void* q, const int32_t* idx,
                                const int32_t* count, int32_t n_cap, float scale, void* out, void* ws,
                                size_t ws_bytes, void* stream);
+
+/*
+ * resa_sparse_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops that
+ * forbid allocation): the same kernels and the same result, bit for bit, with
+ * the split partials in a scratch array of 16 MiB that the library holds in
+ * device memory on each GPU it runs on, until the process ends. Arguments as
+ * for resa_sparse_decode.
+ *  - Calls a configuration whose decode workspace would exceed 16 MiB
+ *    (resa_decode_workspace_size) rejected with RESA_ERR_UNSUPPORTED.
+ *  - Runs on the current device; a non-NULL stream must belong to it
+ *    (RESA_ERR_INVALID otherwise). The first call on a device looks the
+ *    scratch array up (hipGetSymbolAddress); make that call outside graph
+ *    capture.
+ *  - Every call on a GPU shares that GPU's scratch array: calls that may
+ *    overlap on one GPU (different streams, or threads) race, so issue them in
+ *    order on one stream. The partials need no clearing: a call writes every
+ *    slot it reads.
+ *  - Allocates nothing: no hipMalloc or hipFree, no allocating library call.
+ */
+resa_status resa_sparse_decode_noalloc(const resa_cache* cache, const void* q, const int32_t* idx,
+                                       const int32_t* count, int32_t n_cap, float scale, void* out,
+                                       void* stream);
 
 /*
  * Dense rectification (Pith "What carries the argument", "The reading"): the f

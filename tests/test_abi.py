@@ -190,3 +190,18 @@ def test_cache_subset_offsets_pointers():
     assert s.block_table == 0x4000 + 1 * 32 * 4 and s.seq_lens == 0x5000 + 4
     with pytest.raises(ValueError):
         R.CacheSubset(_Parent, 3, 5)
+
+
+def test_noalloc_decode_rejects_a_configuration_beyond_its_scratch(lib):
+    """The no-allocation decode refuses, on the host and before touching any
+    device, a configuration whose split partials exceed its 16 MiB scratch."""
+    c = _cache(batch=2048, num_q_heads=32, num_kv_heads=8)
+    assert lib.resa_decode_workspace_size(ctypes.byref(c), 16) > 16 << 20
+    st = lib.resa_sparse_decode_noalloc(ctypes.byref(c), ctypes.c_void_p(0x6000), ctypes.c_void_p(0x7000),
+                                        ctypes.c_void_p(0x8000), 16, ctypes.c_float(0.1), ctypes.c_void_p(0x9000),
+                                        None)
+    assert st == R.RESA_ERR_UNSUPPORTED
+    assert b"scratch" in lib.resa_last_error()
+    st = lib.resa_sparse_decode_noalloc(ctypes.byref(c), None, ctypes.c_void_p(0x7000), ctypes.c_void_p(0x8000), 16,
+                                        ctypes.c_float(0.1), ctypes.c_void_p(0x9000), None)
+    assert st == R.RESA_ERR_INVALID
