@@ -191,13 +191,32 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(DecodeArgs a) {
   // table row and the page pool, so every load is in bounds; blocks past the
   // count are never used.
   int my_blk = 0, my_page = 0;
+#ifdef RESA_DEBUG_CHECKS
+  int raw_blk = 0, raw_page = 0;
+#endif
   if (lane * kDecWaves < a.bps) {
     const int pos = min(first + wave + kDecWaves * lane, a.n_cap - 1);
     my_blk = min(max(a.idx[gi * a.n_cap + pos], 0), c.maxb - 1);
     my_page = min(max(c.bt[size_t(b) * c.maxb + my_blk], 0), c.num_pages - 1);
+#ifdef RESA_DEBUG_CHECKS
+    raw_blk = a.idx[gi * a.n_cap + pos];
+    raw_page = c.bt[size_t(b) * c.maxb + my_blk];
+#endif
   }
   const int n = a.count[b];
   const int L = c.seq_lens[b];
+#ifdef RESA_DEBUG_CHECKS
+  {  // the indices above are clamped into their arrays whatever they hold; here they are only checked
+    const int M = (L + kBlock - 1) / kBlock;
+    RESA_CHECK(c.dbg, L >= 0 && L <= c.max_seq_len, kChkSeqLen, (void)0);
+    RESA_CHECK(c.dbg, L >= 1, kChkEmpty, (void)0);
+    RESA_CHECK(c.dbg, n >= 0 && n <= a.n_cap, kChkSelection, (void)0);
+    if (lane * kDecWaves < a.bps && first + wave + kDecWaves * lane < min(n, a.n_cap)) {
+      RESA_CHECK(c.dbg, raw_blk >= 0 && raw_blk < M, kChkSelection, (void)0);
+      RESA_CHECK(c.dbg, raw_page >= 0 && raw_page < c.num_pages, kChkPage, (void)0);
+    }
+  }
+#endif
   QRow<T, D> qr[G];
 #pragma unroll
   for (int h = 0; h < G; ++h)
@@ -418,13 +437,32 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_mfma(DecodeArgs a) {
   // block and page ids of this wave's blocks (first + wave + 4 i), clamped
   // into their rows so every load is in bounds; as in the VALU kernel
   int my_blk = 0, my_page = 0;
+#ifdef RESA_DEBUG_CHECKS
+  int raw_blk = 0, raw_page = 0;
+#endif
   if (lane * kDecWaves < a.bps) {
     const int pos = min(first + wave + kDecWaves * lane, a.n_cap - 1);
     my_blk = min(max(a.idx[gi * a.n_cap + pos], 0), c.maxb - 1);
     my_page = min(max(c.bt[size_t(b) * c.maxb + my_blk], 0), c.num_pages - 1);
+#ifdef RESA_DEBUG_CHECKS
+    raw_blk = a.idx[gi * a.n_cap + pos];
+    raw_page = c.bt[size_t(b) * c.maxb + my_blk];
+#endif
   }
   const int n = a.count[b];
   const int L = c.seq_lens[b];
+#ifdef RESA_DEBUG_CHECKS
+  {  // the indices above are clamped into their arrays whatever they hold; here they are only checked
+    const int M = (L + kBlock - 1) / kBlock;
+    RESA_CHECK(c.dbg, L >= 0 && L <= c.max_seq_len, kChkSeqLen, (void)0);
+    RESA_CHECK(c.dbg, L >= 1, kChkEmpty, (void)0);
+    RESA_CHECK(c.dbg, n >= 0 && n <= a.n_cap, kChkSelection, (void)0);
+    if (lane * kDecWaves < a.bps && first + wave + kDecWaves * lane < min(n, a.n_cap)) {
+      RESA_CHECK(c.dbg, raw_blk >= 0 && raw_blk < M, kChkSelection, (void)0);
+      RESA_CHECK(c.dbg, raw_page >= 0 && raw_page < c.num_pages, kChkPage, (void)0);
+    }
+  }
+#endif
   uint4 qk[KS];
   {
     const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (size_t(b) * c.Hq + size_t(g) * G + (h < G ? h : 0)) * D;
@@ -595,7 +633,9 @@ __global__ __launch_bounds__(kCombThreads) void k_decode_combine(DecodeArgs a, v
   const CacheView& c = a.c;
   const int g = blockIdx.x, b = blockIdx.y, h = blockIdx.z, tid = threadIdx.x;
   const size_t gi = size_t(b) * c.Hkv + g;
-  const int live = (a.count[b] + a.bps - 1) / a.bps;
+  // a count above n_cap (a caller's mistake) would name splits past the
+  // partials of this group
+  const int live = (min(a.count[b], a.n_cap) + a.bps - 1) / a.bps;
   const int ch = tid % D, part = tid / D;  // part is wave-uniform
   const float* ml = a.part_ml + (gi * a.splits * G + h) * 2;         // split sp at ml[sp * G * 2]
   const float* acc = a.part_acc + (gi * a.splits * G + h) * D + ch;  // split sp at acc[sp * G * D]

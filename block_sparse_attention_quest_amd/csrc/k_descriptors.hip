@@ -22,7 +22,7 @@ template <typename T, int D, bool NEW>
 __global__ __launch_bounds__(64) void k_refresh_blocks(CacheView c, const void* __restrict__ k_new,
                                                        const void* __restrict__ v_new, int n_new) {
   const int b = blockIdx.z, g = blockIdx.y, lane = threadIdx.x;
-  const int L = c.seq_lens[b];
+  const int L = checked_len(c, b);
   const int lo = n_new > 0 ? max(0, L - n_new) : 0;
   const int j = lo / kBlock + blockIdx.x;
   if (j * kBlock >= L) return;

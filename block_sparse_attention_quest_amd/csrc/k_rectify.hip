@@ -123,9 +123,16 @@ __device__ __forceinline__ void rect_plan(const RectArgs& a) {
 
   const int per_b = (c.B + NT - 1) / NT;
   const int b0 = min(c.B, tid * per_b), b1 = min(c.B, b0 + per_b);
+  // a length read for the plan: checked builds clamp it into f .. max_seq_len,
+  // so that the plan stays within the launch's workgroups and work items
+  auto plan_len = [&](int b) {
+    int L = checked_len(c, b);
+    RESA_CHECK(c.dbg, L >= a.f, kChkRectF, L = max(L, a.f));
+    return L;
+  };
   long long tloc = 0;
   for (int b = b0; b < b1; ++b) {
-    const int L = c.seq_lens[b];
+    const int L = plan_len(b);
     if (IN_LDS) s_len[b] = L;
     tloc += tiles_of(L);
   }
@@ -136,11 +143,11 @@ __device__ __forceinline__ void rect_plan(const RectArgs& a) {
       s_pt[b] = pt;
     else
       a.ptile[b] = pt;
-    pt += tiles_of(IN_LDS ? s_len[b] : c.seq_lens[b]);
+    pt += tiles_of(IN_LDS ? s_len[b] : plan_len(b));
   }
   auto len_of = [&](int b) {
     if constexpr (IN_LDS) return s_len[b];
-    else return c.seq_lens[b];
+    else return plan_len(b);
   };
   auto ptile_of = [&](int b) {
     if constexpr (IN_LDS) return s_pt[b];
@@ -225,7 +232,8 @@ __global__ __launch_bounds__(64) void k_rect_prep(RectArgs a, const void* __rest
   }
   const CacheView& c = a.c;
   const int b = blockIdx.z, g = blockIdx.y, lane = threadIdx.x;
-  const int L = c.seq_lens[b];
+  int L = checked_len(c, b);
+  RESA_CHECK(c.dbg, L >= a.f, kChkRectF, L = max(L, a.f));
   const int j = max(0, L - a.f) / kBlock + blockIdx.x;
   if (j * kBlock >= L) return;
   refresh_block<T, D>(c, k_new, v_new, a.f, b, g, j, L, lane);
@@ -340,7 +348,8 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_rect_mfma(RectArgs a) {
     const int b = it.x, g = it.y & 0xffff, key_lo = it.z, key_hi = it.w;
     const int row0 = (it.y >> 16) * 32 * NWV;       // first row of the item's row tile
     const bool has_rows = row0 + wave * 32 < a.rows;  // wave-uniform
-    const int L = c.seq_lens[b];
+    int L = checked_len(c, b);
+    RESA_CHECK(c.dbg, L >= a.f, kChkRectF, L = max(L, a.f));
     const int ntiles = (key_hi - key_lo + kRectTileKeys - 1) / kRectTileKeys;
     const int first_masked = L - a.f;  // keys from here on are seen by some rows only
 
@@ -349,7 +358,7 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_rect_mfma(RectArgs a) {
     // past the end (the last page repeated)
     const int page0 = key_lo / kBlock, last = (key_hi - 1) / kBlock;
     const int nreq = (ntiles + NS - 1) / NS * NS + NS - 1;  // tiles the pipeline requests
-    for (int i = tid; i < 2 * nreq; i += NT) pages[i] = c.bt[size_t(b) * c.maxb + min(page0 + i, last)];
+    for (int i = tid; i < 2 * nreq; i += NT) pages[i] = checked_page(c, b, min(page0 + i, last));
 
     // this lane's query row as MFMA B operands (S^T = K Q^T)
     bf16x8_t qreg[KSTEPS];
@@ -611,6 +620,7 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_rect_mfma(RectArgs a) {
     }
   }
 }
+
 #undef RESA_STAGE_DECL
 
 template <typename T>
@@ -691,7 +701,8 @@ __global__ __launch_bounds__(64) void k_rect_valu(RectArgs a, void* __restrict__
   const CacheView& c = a.c;
   const int h = blockIdx.x, i = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
   const int g = h / c.G;
-  const int L = c.seq_lens[b];
+  int L = checked_len(c, b);
+  RESA_CHECK(c.dbg, L >= a.f, kChkRectF, L = max(L, a.f));
   const int P = L - a.f + i;  // last visible position
   __shared__ float qs[D];
   __shared__ float ps[64];
@@ -705,7 +716,7 @@ __global__ __launch_bounds__(64) void k_rect_valu(RectArgs a, void* __restrict__
     const int t = t0 + lane;
     float x = -__builtin_inff();
     if (t <= P) {
-      const int page = c.bt[size_t(b) * c.maxb + (t >> 4)];
+      const int page = checked_page(c, b, t >> 4);
       const size_t row = ((size_t(page) * c.Hkv + g) * kBlock + (t & 15)) * D;
       float sdot = 0.f;
       for (int ch = 0; ch < D; ++ch) sdot = fmaf(qs[ch], load_elem<T>(c.k, row + ch), sdot);
@@ -730,7 +741,7 @@ __global__ __launch_bounds__(64) void k_rect_valu(RectArgs a, void* __restrict__
     for (int e = 0; e < D / 64; ++e) acc[e] *= alpha;
     for (int k = 0; k < nt; ++k) {
       const int tt = t0 + k;
-      const int page = c.bt[size_t(b) * c.maxb + (tt >> 4)];
+      const int page = checked_page(c, b, tt >> 4);
       const size_t vt = (size_t(page) * c.Hkv + g) * D * kBlock + (tt & 15);  // channel-major V tile
 #pragma unroll
       for (int e = 0; e < D / 64; ++e)

@@ -123,7 +123,8 @@ __global__ __launch_bounds__(kScoreThreads) void k_score(CacheView c, const void
   constexpr int ROWS = kScoreChunk / (4 * BPW);
   const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int L = c.seq_lens[b];
+  const int L = checked_len(c, b);
+  RESA_CHECK(c.dbg, L >= 1, kChkEmpty, (void)0);
   const int M = (L + kBlock - 1) / kBlock;
   if (append && chunk == int(gridDim.x) - 1) {
     if (wave == 0 && L > 0) refresh_block<T, D>(c, k_new, v_new, 1, b, g, (L - 1) / kBlock, L, lane);
@@ -147,7 +148,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_score(CacheView c, const void
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) {
     jr[r] = chunk * kScoreChunk + (r * 4 + wave) * BPW + slot;
-    page[r] = c.bt[size_t(b) * c.maxb + (jr[r] < Mo ? jr[r] : 0)];
+    page[r] = checked_page(c, b, jr[r] < Mo ? jr[r] : 0);
   }
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) {
@@ -515,13 +516,15 @@ template <int EMAX>
 __global__ __launch_bounds__(kTopnThreads) void k_topn(const uint64_t* __restrict__ keys, int stride,
                                                        const int32_t* __restrict__ seq_lens, int Hkv,
                                                        resa_select_params p, int32_t* __restrict__ idx,
-                                                       int32_t* __restrict__ count, int n_cap) {
+                                                       int32_t* __restrict__ count, int n_cap, int max_len,
+                                                       int* dbg) {
   __shared__ TopnShared sm;
   const int g = blockIdx.x, b = blockIdx.y;
   const size_t gi = size_t(b) * Hkv + g;
   RegKeys<EMAX> rk;
   rk.load(keys + gi * stride, stride);  // issued before the sequence length arrives
-  const int L = seq_lens[b];
+  int L = seq_lens[b];
+  RESA_CHECK(dbg, L >= 0 && L <= max_len, kChkSeqLen, L = min(max(L, 0), max_len));
   const int M = (L + kBlock - 1) / kBlock;
   const int n = select_count(M, p);
   if (g == 0 && threadIdx.x == 0) count[b] = n;
@@ -535,7 +538,7 @@ hipError_t launch_topn(const CacheView& c, const resa_select_params& p, int32_t*
   dim3 grid(c.Hkv, c.B);
   const int e = (mmax + kTopnThreads - 1) / kTopnThreads;
 #define RESA_TOPN(E) hipLaunchKernelGGL(k_topn<E>, grid, dim3(kTopnThreads), 0, s, keys, stride, c.seq_lens, \
-                                        c.Hkv, p, idx, count, n_cap)
+                                        c.Hkv, p, idx, count, n_cap, c.max_seq_len, c.dbg)
   // every thread handles EMAX keys: exact up to 18 (256K context), then
   // coarser steps
   switch (e) {

@@ -71,7 +71,7 @@ __device__ __forceinline__ void refresh_block(const CacheView& c, const void* __
   const int c0 = lane * CPL;
   const bool has_new = NEW && n_new > 0 && k_new != nullptr;
   const int lo = n_new > 0 ? max(0, L - n_new) : 0;
-  const int page = c.bt[size_t(b) * c.maxb + j];
+  const int page = checked_page(c, b, j);
   const int valid = min(kBlock, L - j * kBlock);
   const size_t row0 = (size_t(page) * c.Hkv + g) * kBlock;  // token-row index of slot 0
   const int first_new = has_new ? lo - j * kBlock : kBlock;  // slot of the first fresh row

@@ -1,6 +1,8 @@
 // C ABI of libresa.so: argument validation, workspace sizing and launch order.
 // All checks run on the host before anything is launched; nothing here reads
-// device memory or synchronises with the device.
+// device memory or synchronises with the device, except in checked builds
+// (RESA_DEBUG_CHECKS), where each call waits for its stream and reads the word
+// the kernels' precondition checks set.
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -82,6 +84,7 @@ resa_status check_cache(const resa_cache* c, resa::CacheView* v) {
   v->desc = c->desc;
   v->bt = c->block_table;
   v->seq_lens = c->seq_lens;
+  v->dbg = nullptr;
   return RESA_OK;
 }
 
@@ -93,34 +96,97 @@ resa_status check_params(const resa_select_params* p) {
   return RESA_OK;
 }
 
+constexpr int kMaxDevices = 64;
+
+// The device address of a __device__ array on the current device `dev`,
+// looked up once per device (each GPU holds its own copy of the array).
+resa_status symbol_on_device(const void* sym, const char* name, std::atomic<void*>* cache, int dev, void** out) {
+  static std::mutex mu;
+  void* p = cache[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(mu);
+    p = cache[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      const hipError_t e = hipGetSymbolAddress(&p, sym);
+      if (e != hipSuccess) return fail(RESA_ERR_HIP, "hipGetSymbolAddress(%s): %s", name, hipGetErrorString(e));
+      if (!p) return fail(RESA_ERR_HIP, "hipGetSymbolAddress(%s) returned NULL", name);
+      cache[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return RESA_OK;
+}
+
+resa_status current_device(int* dev) {
+  const hipError_t e = hipGetDevice(dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (*dev < 0 || *dev >= kMaxDevices) return fail(RESA_ERR_UNSUPPORTED, "device %d (at most %d devices)", *dev, kMaxDevices);
+  return RESA_OK;
+}
+
 // Scratch of resa_sparse_decode_noalloc: the decode's split partials live in
 // this array instead of a caller workspace. Each GPU the library runs on holds
 // its own copy until the process ends; host code never uses the array's name as
 // an address, only the device pointer hipGetSymbolAddress returns for it.
 constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
 static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
-
-constexpr int kMaxDevices = 64;
 std::atomic<void*> g_scratch_ptr[kMaxDevices];
-std::mutex g_scratch_mu;
 
-// The scratch array's address on `dev` (the current device), looked up once
-// per device.
-resa_status scratch_on_device(int dev, void** out) {
-  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
-  if (!p) {
-    std::lock_guard<std::mutex> lock(g_scratch_mu);
-    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
-    if (!p) {
-      const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
-      if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
-      if (!p) return fail(RESA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
-      g_scratch_ptr[dev].store(p, std::memory_order_release);
-    }
-  }
-  *out = p;
+#ifdef RESA_DEBUG_CHECKS
+// Checked builds: the word the kernels' precondition checks set (one per
+// device). Every launching call attaches it to the cache view, then waits for
+// its stream and turns a set bit into RESA_ERR_INVALID. Calls that overlap on
+// one device share the word, so a failed check may be reported by another of
+// them; checked builds are for testing, one stream at a time.
+static __device__ int debug_word[1];
+std::atomic<void*> g_debug_ptr[kMaxDevices];
+
+resa_status debug_attach(resa::CacheView* v) {
+  int dev = -1;
+  resa_status st = current_device(&dev);
+  if (st != RESA_OK) return st;
+  void* p = nullptr;
+  if ((st = symbol_on_device(HIP_SYMBOL(debug_word), "debug_word", g_debug_ptr, dev, &p)) != RESA_OK) return st;
+  v->dbg = static_cast<int*>(p);
   return RESA_OK;
 }
+
+resa_status debug_collect(resa_status st, hipStream_t s, const resa::CacheView& v) {
+  if (st != RESA_OK) return st;
+  // under graph capture nothing runs yet and the stream cannot be waited on:
+  // a check that fails on a replay is reported by the next uncaptured call
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(s, &cap);
+  if (e != hipSuccess) return hip_status(e, "hipStreamIsCapturing (checked build)");
+  if (cap != hipStreamCaptureStatusNone) return RESA_OK;
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_status(e, "hipStreamSynchronize (checked build)");
+  int word = 0;
+  if ((e = hipMemcpy(&word, v.dbg, sizeof(int), hipMemcpyDeviceToHost)) != hipSuccess)
+    return hip_status(e, "reading the check word");
+  if (!word) return RESA_OK;
+  const int zero = 0;
+  if ((e = hipMemcpy(v.dbg, &zero, sizeof(int), hipMemcpyHostToDevice)) != hipSuccess)
+    return hip_status(e, "clearing the check word");
+  return fail(RESA_ERR_INVALID, "device-side precondition check failed:%s%s%s%s%s",
+              word & resa::kChkSeqLen ? " seq_lens[b] outside 0 .. max_seq_len;" : "",
+              word & resa::kChkPage ? " a held block's block_table entry outside 0 .. num_pages - 1;" : "",
+              word & resa::kChkEmpty ? " an empty sequence where a token is needed;" : "",
+              word & resa::kChkSelection ? " count above n_cap or a selected block outside the sequence;" : "",
+              word & resa::kChkRectF ? " f above seq_lens[b];" : "");
+}
+#define RESA_DEBUG_ATTACH(v)                              \
+  do {                                                    \
+    const resa_status ast = debug_attach(&(v));           \
+    if (ast != RESA_OK) return ast;                       \
+  } while (0)
+#define RESA_DEBUG_COLLECT(expr, stream, v) debug_collect((expr), (stream), (v))
+#else
+#define RESA_DEBUG_ATTACH(v) \
+  do {                       \
+  } while (0)
+#define RESA_DEBUG_COLLECT(expr, stream, v) (expr)
+#endif
 
 int n_for(int M, const resa_select_params* p) {
   int n = (int)ceil((double)M * p->r);
@@ -167,8 +233,9 @@ resa_status resa_update_descriptors(const resa_cache* cache, const void* k_new, 
   if (n_new > v.max_seq_len) return fail(RESA_ERR_INVALID, "n_new %d exceeds max_seq_len %d", n_new, v.max_seq_len);
   if ((st = check_aligned16("k_new and v_new", {k_new, v_new})) != RESA_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  RESA_DEBUG_ATTACH(v);
   const hipError_t e = n_new == 0 ? resa::launch_rebuild(v, s) : resa::launch_update_tail(v, k_new, v_new, n_new, s);
-  return hip_status(e, "resa_update_descriptors");
+  return RESA_DEBUG_COLLECT(hip_status(e, "resa_update_descriptors"), s, v);
 }
 
 resa_status resa_select_blocks(const resa_cache* cache, const void* q, const resa_select_params* params,
@@ -185,8 +252,11 @@ resa_status resa_select_blocks(const resa_cache* cache, const void* q, const res
   if (n_cap < need_cap) return fail(RESA_ERR_INVALID, "n_cap %d is below resa_n_cap() = %d", n_cap, need_cap);
   const size_t need = resa::select_ws_bytes(v);
   if (!ws || ws_bytes < need) return fail(RESA_ERR_WORKSPACE, "select workspace %zu < %zu bytes", ws_bytes, need);
-  return hip_status(resa::launch_select(v, q, *params, idx, count, n_cap, ws, static_cast<hipStream_t>(stream)),
-                    "resa_select_blocks");
+  RESA_DEBUG_ATTACH(v);
+  return RESA_DEBUG_COLLECT(
+      hip_status(resa::launch_select(v, q, *params, idx, count, n_cap, ws, static_cast<hipStream_t>(stream)),
+                 "resa_select_blocks"),
+      static_cast<hipStream_t>(stream), v);
 }
 
 resa_status resa_append_select(const resa_cache* cache, const void* k_new, const void* v_new, const void* q,
@@ -204,9 +274,11 @@ resa_status resa_append_select(const resa_cache* cache, const void* k_new, const
   if (n_cap < need_cap) return fail(RESA_ERR_INVALID, "n_cap %d is below resa_n_cap() = %d", n_cap, need_cap);
   const size_t need = resa::select_ws_bytes(v);
   if (!ws || ws_bytes < need) return fail(RESA_ERR_WORKSPACE, "select workspace %zu < %zu bytes", ws_bytes, need);
-  return hip_status(resa::launch_append_select(v, k_new, v_new, q, *params, idx, count, n_cap, ws,
-                                               static_cast<hipStream_t>(stream)),
-                    "resa_append_select");
+  RESA_DEBUG_ATTACH(v);
+  return RESA_DEBUG_COLLECT(hip_status(resa::launch_append_select(v, k_new, v_new, q, *params, idx, count, n_cap, ws,
+                                                                  static_cast<hipStream_t>(stream)),
+                                       "resa_append_select"),
+                            static_cast<hipStream_t>(stream), v);
 }
 
 resa_status resa_sparse_decode(const resa_cache* cache, const void* q, const int32_t* idx,
@@ -222,8 +294,11 @@ resa_status resa_sparse_decode(const resa_cache* cache, const void* q, const int
   if (!(scale > 0.f) || !isfinite(scale)) return fail(RESA_ERR_INVALID, "scale must be positive and finite");
   const size_t need = resa::decode_ws_bytes(v, n_cap);
   if (!ws || ws_bytes < need) return fail(RESA_ERR_WORKSPACE, "decode workspace %zu < %zu bytes", ws_bytes, need);
-  return hip_status(resa::launch_decode(v, q, idx, count, n_cap, scale, out, ws, static_cast<hipStream_t>(stream)),
-                    "resa_sparse_decode");
+  RESA_DEBUG_ATTACH(v);
+  return RESA_DEBUG_COLLECT(
+      hip_status(resa::launch_decode(v, q, idx, count, n_cap, scale, out, ws, static_cast<hipStream_t>(stream)),
+                 "resa_sparse_decode"),
+      static_cast<hipStream_t>(stream), v);
 }
 
 resa_status resa_sparse_decode_noalloc(const resa_cache* cache, const void* q, const int32_t* idx,
@@ -242,19 +317,20 @@ resa_status resa_sparse_decode_noalloc(const resa_cache* cache, const void* q, c
     return fail(RESA_ERR_UNSUPPORTED, "the decode needs %zu bytes of scratch; resa_sparse_decode_noalloc holds %zu",
                 need, kNoAllocScratchBytes);
   int dev = -1;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
-  if (dev < 0 || dev >= kMaxDevices) return fail(RESA_ERR_UNSUPPORTED, "device %d (at most %d devices)", dev, kMaxDevices);
+  if ((st = current_device(&dev)) != RESA_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (s) {
     hipDevice_t sdev = -1;
-    if ((e = hipStreamGetDevice(s, &sdev)) != hipSuccess) return hip_status(e, "hipStreamGetDevice");
+    const hipError_t e = hipStreamGetDevice(s, &sdev);
+    if (e != hipSuccess) return hip_status(e, "hipStreamGetDevice");
     if (sdev != dev)
       return fail(RESA_ERR_INVALID, "stream belongs to device %d but device %d is current", int(sdev), dev);
   }
   void* ws = nullptr;
-  if ((st = scratch_on_device(dev, &ws)) != RESA_OK) return st;
-  return hip_status(resa::launch_decode(v, q, idx, count, n_cap, scale, out, ws, s), "resa_sparse_decode_noalloc");
+  if ((st = symbol_on_device(HIP_SYMBOL(scratch), "scratch", g_scratch_ptr, dev, &ws)) != RESA_OK) return st;
+  RESA_DEBUG_ATTACH(v);
+  return RESA_DEBUG_COLLECT(
+      hip_status(resa::launch_decode(v, q, idx, count, n_cap, scale, out, ws, s), "resa_sparse_decode_noalloc"), s, v);
 }
 
 resa_status resa_rectify(const resa_cache* cache, const void* q, const void* k_new, const void* v_new,
@@ -271,8 +347,11 @@ resa_status resa_rectify(const resa_cache* cache, const void* q, const void* k_n
   if (!ws || ws_bytes < need) return fail(RESA_ERR_WORKSPACE, "rectify workspace %zu < %zu bytes", ws_bytes, need);
   // the write and refresh come first: rectified rows attend to the rectified
   // K/V of earlier rows
-  return hip_status(resa::launch_rectify(v, q, k_new, v_new, f, scale, out, ws, static_cast<hipStream_t>(stream)),
-                    "resa_rectify");
+  RESA_DEBUG_ATTACH(v);
+  return RESA_DEBUG_COLLECT(
+      hip_status(resa::launch_rectify(v, q, k_new, v_new, f, scale, out, ws, static_cast<hipStream_t>(stream)),
+                 "resa_rectify"),
+      static_cast<hipStream_t>(stream), v);
 }
 
 const char* resa_last_error(void) { return g_err; }

@@ -105,7 +105,50 @@ struct CacheView {
   void* desc;
   const int32_t* bt;
   const int32_t* seq_lens;
+  int* dbg;   // checked builds: the device word the precondition checks set (NULL otherwise)
 };
+
+// ---------------------------------------------------------------------------
+// Device-side precondition checks (built with RESA_DEBUG_CHECKS only). A
+// kernel that finds a caller precondition broken sets its bit in the device
+// word (c.dbg) and clamps the offending value into range, so that every access
+// stays in bounds and every workgroup still reaches its barriers (the results
+// are then meaningless); the entry point synchronises its stream and returns
+// RESA_ERR_INVALID. Release builds compile every check away.
+// ---------------------------------------------------------------------------
+enum DebugCheck {
+  kChkSeqLen = 1,     // seq_lens[b] outside 0 .. max_seq_len
+  kChkPage = 2,       // a held block's block_table entry outside 0 .. num_pages - 1
+  kChkEmpty = 4,      // seq_lens[b] < 1 where selection or decoding needs a token
+  kChkSelection = 8,  // count[b] > n_cap, or a selected block outside 0 .. M_b - 1
+  kChkRectF = 16,     // f > seq_lens[b] in a rectification
+};
+#ifdef RESA_DEBUG_CHECKS
+#define RESA_CHECK(dbg, cond, bit, fix)          \
+  do {                                           \
+    if (!(cond)) {                               \
+      atomicOr((dbg), int(bit));                 \
+      fix;                                       \
+    }                                            \
+  } while (0)
+#else
+#define RESA_CHECK(dbg, cond, bit, fix) \
+  do {                                  \
+  } while (0)
+#endif
+
+// A sequence length read for a kernel, checked against the cache capacity.
+__device__ __forceinline__ int checked_len(const CacheView& c, int b) {
+  int L = c.seq_lens[b];
+  RESA_CHECK(c.dbg, L >= 0 && L <= c.max_seq_len, kChkSeqLen, L = min(max(L, 0), c.max_seq_len));
+  return L;
+}
+// A block-table entry of a held block, checked against the page pool.
+__device__ __forceinline__ int checked_page(const CacheView& c, int b, int j) {
+  int page = c.bt[size_t(b) * c.maxb + j];
+  RESA_CHECK(c.dbg, page >= 0 && page < c.num_pages, kChkPage, page = 0);
+  return page;
+}
 
 hipError_t launch_update_tail(const CacheView& c, const void* k_new, const void* v_new, int n_new,
                               hipStream_t s);

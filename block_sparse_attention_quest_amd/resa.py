@@ -51,11 +51,13 @@ def lib_path() -> str:
 
 
 def load(path: Optional[str] = None) -> ctypes.CDLL:
-    """Load libresa.so (once). Raises if it has not been built."""
+    """Load libresa.so (once; the RESA_LIB environment variable may name
+    another build of it, e.g. the checked build). Raises if it has not been
+    built."""
     global _lib
     if _lib is not None:
         return _lib
-    p = path or _LIB_PATH
+    p = path or os.environ.get("RESA_LIB") or _LIB_PATH
     if not os.path.exists(p):
         raise RuntimeError(f"{p} is missing: build it with `python -m block_sparse_attention_quest_amd.build`")
     lib = ctypes.CDLL(p)
