@@ -182,6 +182,115 @@ class ResaRunner:
                     on_rectify(t, ro)
 
 
+class Lanes:
+    """The batch of a ResaRunner cut into contiguous sequence ranges ("lanes"),
+    each issuing its calls on a HIP stream of its own, with its own workspace
+    and its slices of the runner's index, count and output buffers.
+
+    Sequences are independent within one attention layer, so the lanes'
+    kernels may run at the same time. What that buys is overlap of unlike
+    work: the top-n selection and the merge of the decode splits are
+    latency-bound (few workgroups, dependent steps), the scoring and the
+    sparse decode stream HBM. With `stagger`, lane i's append + selection
+    of a step starts after lane i - 1's has finished, so the lanes run a phase
+    apart and one lane's latency-bound kernels run under another's streaming
+    ones. `phases` gives each lane its own rectification phase (continuous
+    batching: lane i rectifies after step t when (t + 1 + phases[i]) % f == 0
+    and t >= f - 1), so one lane's rectification overlaps the other lanes'
+    decode steps.
+
+    Host work per call is kept small: the calls go straight to the C ABI
+    with argument lists prepared at construction (pointers of every step's
+    inputs), since at batch sizes where a step takes tens of microseconds the
+    host issues several calls per step.
+    """
+
+    def __init__(self, runner: "ResaRunner", ranges, stagger: bool = True, phases=None):
+        import ctypes
+        self.r = runner
+        self.ranges = [(int(a), int(b)) for a, b in ranges]
+        bs = [x for rg in self.ranges for x in range(*rg)]
+        if bs != list(range(runner.w.batch)):
+            raise ValueError(f"lanes {self.ranges} must cut the batch 0 .. {runner.w.batch} into contiguous ranges")
+        self.stagger = stagger
+        self.phases = list(phases) if phases is not None else [0] * len(self.ranges)
+        w, c = runner.w, runner.cache
+        self.lib = R.load()
+        self.streams = [torch.cuda.Stream(device=runner.device) for _ in self.ranges]
+        self.events = [torch.cuda.Event() for _ in self.ranges]
+        self.views = [R.CacheSubset(c, b0, b1) for b0, b1 in self.ranges]
+        self.structs = [v.struct for v in self.views]
+        self.ws = []
+        for v in self.views:
+            n = max(R.resa_select_workspace_size(v), R.resa_decode_workspace_size(v, runner.n_cap),
+                    R.resa_rectify_workspace_size(v, w.f) if w.f > 0 else 0)
+            self.ws.append(R.workspace(n, runner.device))
+        self.scale = ctypes.c_float(runner.scale)
+        self.params = ctypes.byref(runner.params)
+        self.rect_outs = [torch.empty(b1 - b0, max(w.f, 1), w.num_q_heads, w.head_dim, dtype=w.torch_dtype,
+                                      device=runner.device) for b0, b1 in self.ranges]
+        si = runner.step_inputs
+        self.args = []  # per lane: per step (k, v, q) pointers, then the fixed pointers
+        for (b0, b1), ws in zip(self.ranges, self.ws):
+            steps = [(si["k"][t][b0:b1].data_ptr(), si["v"][t][b0:b1].data_ptr(), si["q"][t][b0:b1].data_ptr())
+                     for t in range(runner.steps)] if si else []
+            self.args.append({"steps": steps, "idx": runner.idx[b0:b1].data_ptr(),
+                              "count": runner.count[b0:b1].data_ptr(), "out": runner.out[b0:b1].data_ptr(),
+                              "ws": ws.data_ptr(), "ws_bytes": ws.numel()})
+
+    def _check(self, st):
+        if st != R.RESA_OK:
+            raise R.ResaError(st, self.lib.resa_last_error().decode())
+
+    def fork(self) -> None:
+        """Every lane stream waits for the work queued so far on the current stream."""
+        cur = torch.cuda.current_stream()
+        for s in self.streams:
+            s.wait_stream(cur)
+
+    def join(self) -> None:
+        """The current stream waits for every lane."""
+        cur = torch.cuda.current_stream()
+        for s in self.streams:
+            cur.wait_stream(s)
+
+    def due(self, i: int, t: int) -> bool:
+        f = self.r.w.f
+        return f > 0 and t >= f - 1 and (t + 1 + self.phases[i]) % f == 0
+
+    def step(self, t: int, rect_in: Optional[Dict[int, tuple]] = None, keep=None) -> None:
+        """Decode step t on every lane (append + selection, then the sparse
+        decode), then the rectification of the lanes that are due, using
+        rect_in[t] = (q, k, v) of the whole batch (sliced per lane). With
+        `keep`, a callable (lane, t, out, rect_out) is run on the lane's stream
+        after its calls (e.g. copies of the outputs)."""
+        import ctypes
+        r, lib = self.r, self.lib
+        lens = r.lens[t + 1].data_ptr()
+        for i, ((b0, b1), st, a, s) in enumerate(zip(self.ranges, self.structs, self.args, self.streams)):
+            st.seq_lens = lens + 4 * b0
+            if self.stagger and i > 0:
+                s.wait_event(self.events[i - 1])
+            k, v, q = a["steps"][t]
+            self._check(lib.resa_append_select(ctypes.byref(st), k, v, q, self.params, a["idx"], a["count"], r.n_cap,
+                                               a["ws"], a["ws_bytes"], s.cuda_stream))
+            if self.stagger:
+                self.events[i].record(s)
+        for i, ((b0, b1), st, a, s) in enumerate(zip(self.ranges, self.structs, self.args, self.streams)):
+            q = a["steps"][t][2]
+            self._check(lib.resa_sparse_decode(ctypes.byref(st), q, a["idx"], a["count"], r.n_cap, self.scale,
+                                               a["out"], a["ws"], a["ws_bytes"], s.cuda_stream))
+            rout = None
+            if rect_in is not None and self.due(i, t):
+                rq, rk, rv = (x[b0:b1] for x in rect_in[t])
+                rout = self.rect_outs[i]
+                self._check(lib.resa_rectify(ctypes.byref(st), rq.data_ptr(), rk.data_ptr(), rv.data_ptr(), r.w.f,
+                                             self.scale, rout.data_ptr(), a["ws"], a["ws_bytes"], s.cuda_stream))
+            if keep is not None:
+                with torch.cuda.stream(s):
+                    keep(i, t, r.out[b0:b1], rout)
+
+
 class ChunkedPrefill:
     """Dense causal prefill through the rectification call ("Rectified Sparse
     Attention": rectification re-encodes recent tokens with the dense pass;
