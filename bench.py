@@ -171,6 +171,111 @@ def cpu_baseline(w, first_step, budget_s):
                        f"NumPy steps one")}
 
 
+def oracle_sweep(args):
+    """The oracle as it stands, timed on the host for every workload: all 64
+    steps of the tiny fp32 schedule (rectifications included), and for each
+    large workload one decode step (append, descriptor, selection and sparse
+    decode of every (sequence, KV head) group) and one rectification event
+    (every query row over its causal prefix), each measured on a bounded
+    sample (whole groups, whole rows) and scaled to the batch. Prints one JSON
+    line per workload and a markdown table."""
+    import numpy as np
+    from block_sparse_attention_quest_amd import workloads as W
+    from oracle import resa_oracle as O
+
+    cores = len(os.sched_getaffinity(0))
+    budget = args.cpu_seconds
+    rows_out = []
+
+    # the tiny schedule, whole
+    w = W.tiny_fp32()
+    bt = W.block_table(w).numpy()
+    kp = np.zeros((w.num_pages, 1, 16, w.head_dim))
+    vp = np.zeros_like(kp)
+    k0, v0 = W.prefill_kv(w, 0, 0)
+    for t in range(w.prefill_lens[0]):
+        kp[bt[0, t // 16], 0, t % 16] = k0[t].double().numpy()
+        vp[bt[0, t // 16], 0, t % 16] = v0[t].double().numpy()
+    cache = O.PagedCache(kp, vp, np.zeros((w.num_pages, 1, 2, w.head_dim)), bt, list(w.prefill_lens))
+    cache.rebuild()
+    steps = [(W.query(w, t).double().numpy(),) + tuple(x.double().numpy() for x in W.append_kv(w, t))
+             for t in range(w.steps)]
+    rect = {t: tuple(x.double().numpy() for x in W.rectify_inputs(w, t)) for t in W.rectify_steps(w)}
+    t0 = time.perf_counter()
+    O.resa_loop(cache, w.steps, w.f, w.n_min, w.r, w.n_local, 1.0 / math.sqrt(w.head_dim),
+                step_inputs=lambda t: steps[t], rectify_inputs=lambda t: rect[t])
+    sec = time.perf_counter() - t0
+    rows_out.append({"workload": w.name, "oracle_steps_per_s": round(w.steps / sec, 2),
+                     "sample": f"all {w.steps} steps and {len(rect)} rectifications, {sec:.2f} s"})
+    print(json.dumps(rows_out[-1]), flush=True)
+
+    for make in (W.llama8b_32k, W.gqa_128k, W.long_256k, lambda: W.long_256k(f=64), W.rectify_mixed):
+        w = make()
+        G, d = w.group, w.head_dim
+        scale = 1.0 / math.sqrt(d)
+        groups = [(b, g) for b in range(w.batch) for g in range(w.num_kv_heads)]
+        np.random.default_rng(w.seed).shuffle(groups)
+        decode = w.steps > 0
+        t_dec, t_row = [], []
+        q_step = W.query(w, 0).double().numpy() if decode else None
+        rq = (W.rectify_only_inputs(w)[0] if not decode else W.rectify_inputs(w, w.f - 1)[0]).double().numpy()
+        t_start = time.perf_counter()
+        for (b, g) in groups:
+            k0, v0 = W.prefill_kv(w, b, g)
+            K, V = k0.double().numpy(), v0.double().numpy()
+            if decode:
+                k, v = W.append_kv(w, 0)
+                K = np.concatenate([K, k[b, g][None].double().numpy()])
+                V = np.concatenate([V, v[b, g][None].double().numpy()])
+                kmin, kmax = O.block_descriptors(K[:len(K) - (len(K) - 1) % 16 - 1])  # the blocks before the newest
+                qg = q_step[b, g * G:(g + 1) * G]
+                M = O.num_blocks(len(K))
+                best = math.inf
+                for _ in range(2):  # the faster of two: the input draws' thread pool may still be spinning
+                    s0 = time.perf_counter()
+                    lmin, lmax = O.block_descriptors(K[(M - 1) * 16:])
+                    km = np.concatenate([kmin[:M - 1], lmin])
+                    kx = np.concatenate([kmax[:M - 1], lmax])
+                    s = O.block_upper_bounds(O.pooled_query(qg), km, kx)
+                    sel = O.select_blocks(s, O.active_block_count(M, w.n_min, w.r), w.n_local)
+                    O.sparse_decode_group(qg, K, V, sel, scale)
+                    best = min(best, time.perf_counter() - s0)
+                t_dec.append(best)
+            # rectified rows of this group: the last row of the f (the longest prefix)
+            L = len(K) + (w.f if not decode else 0)
+            if not decode:
+                k, v = W.rectify_only_inputs(w)[1:]
+                K = np.concatenate([K, k[b, :, g].double().numpy()])
+                V = np.concatenate([V, v[b, :, g].double().numpy()])
+            best = math.inf
+            for _ in range(2):
+                s1 = time.perf_counter()
+                O.causal_rows(rq[b, -1:, g * G], K, V, len(K) - 1, scale)
+                best = min(best, time.perf_counter() - s1)
+            t_row.append(best)
+            if time.perf_counter() - t_start > budget:
+                break
+        # every one of a group's f * G rows sees about as many keys as its
+        # last row (f is small against the context)
+        rect_s = float(np.mean(t_row)) * w.f * G * len(groups)
+        row = {"workload": f"{w.name} (f {w.f})", "oracle_rectify_s": round(rect_s, 2),
+               "sample": (f"{len(t_row)} of {len(groups)} groups; rectification: the last row of each sampled "
+                          f"group timed, scaled to all {w.batch * w.f * w.num_q_heads} rows")}
+        if decode:
+            dec_s = float(np.mean(t_dec)) * len(groups)
+            row["oracle_decode_step_s"] = round(dec_s, 3)
+            row["oracle_steps_per_s_amortised"] = round(1.0 / (dec_s + rect_s / w.f), 3)
+            row["sample"] += f"; decode: {len(t_dec)} groups' steps timed, scaled to {len(groups)}"
+        rows_out.append(row)
+        print(json.dumps(row), flush=True)
+    print(f"| workload | oracle decode step (s) | oracle rectification event (s) | oracle steps/s | sample |")
+    print("|---|---|---|---|---|")
+    for r in rows_out:
+        print(f"| {r['workload']} | {r.get('oracle_decode_step_s', '-')} | {r.get('oracle_rectify_s', '-')} | "
+              f"{r.get('oracle_steps_per_s', r.get('oracle_steps_per_s_amortised', '-'))} | {r['sample']} |")
+    print(f"host threads available: {cores}")
+
+
 # ---------------------------------------------------------------------------
 
 def rectify_only(w, args):
@@ -362,6 +467,11 @@ def main():
                     help="replay the timed steps from one HIP graph (no per-launch host work)")
     ap.add_argument("--unfused-append", action="store_true",
                     help="append with resa_update_descriptors, then resa_select_blocks (two calls)")
+    ap.add_argument("--lanes", type=int, default=1,
+                    help="cut the batch into this many sequence ranges, each issuing its calls on its own stream")
+    ap.add_argument("--no-stagger", action="store_true", help="with --lanes: do not start the lanes a phase apart")
+    ap.add_argument("--oracle-sweep", action="store_true",
+                    help="time the CPU oracle on every workload (bounded samples; no GPU work)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -371,6 +481,8 @@ def main():
         print("bench.py measures one GPU only: the hot path here is the per-GPU kernel; "
               "sharding across GPUs is a design note, not built. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.oracle_sweep:
+        return oracle_sweep(args)
 
     import torch
     from block_sparse_attention_quest_amd import resa as R
@@ -417,13 +529,27 @@ def main():
         torch.cuda.synchronize()
         del src, dst, junk
 
+    lanes = None
+    if args.lanes > 1:
+        from block_sparse_attention_quest_amd.schedule import Lanes
+        if w.batch % args.lanes:
+            sys.exit(f"--lanes {args.lanes} does not divide the batch of {w.batch}")
+        per = w.batch // args.lanes
+        lanes = Lanes(r, [(i * per, (i + 1) * per) for i in range(args.lanes)], stagger=not args.no_stagger)
+
     def step(t):
         r.decode_step(t)
         if t in rect_in:
             r.rectify(t, *rect_in[t])
 
-    for t in range(Wu):
-        step(t)
+    if lanes is not None:
+        lanes.fork()
+        for t in range(Wu):
+            lanes.step(t, rect_in)
+        lanes.join()
+    else:
+        for t in range(Wu):
+            step(t)
     torch.cuda.synchronize()
 
     def step_calls(t, ev=None):
@@ -459,7 +585,20 @@ def main():
     # --graph the K steps are recorded into one HIP graph first (recording runs
     # nothing) and the timed region is its replay ----
     graph = None
-    if args.graph:
+    if args.graph and lanes is not None:
+        # every lane's stream joins the capture through fork() and leaves it
+        # through join(); the graph holds their calls as parallel branches
+        graph = torch.cuda.CUDAGraph()
+        cs = torch.cuda.Stream()
+        cs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.graph(graph, stream=cs):
+            lanes.fork()
+            for i in range(K):
+                lanes.step(Wu + i, rect_in)
+            lanes.join()
+        torch.cuda.current_stream().wait_stream(cs)
+        torch.cuda.synchronize()
+    elif args.graph:
         graph, _, _ = r.capture(Wu, Wu + K, {t: x for t, x in rect_in.items() if Wu <= t < Wu + K})
         torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -467,6 +606,11 @@ def main():
     e0.record(stream)
     if graph is not None:
         graph.replay()
+    elif lanes is not None:
+        lanes.fork()
+        for i in range(K):
+            lanes.step(Wu + i, rect_in)
+        lanes.join()
     else:
         for i in range(K):
             step_calls(Wu + i)
@@ -592,7 +736,10 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "launch": "one HIP graph of the timed steps" if args.graph else "calls from the host, one by one",
+        "launch": ("one HIP graph of the timed steps" if args.graph else
+                   f"{args.lanes} lanes of {w.batch // args.lanes} sequences, each on its own stream"
+                   f"{'' if args.no_stagger else ', a phase apart'}" if lanes is not None else
+                   "calls from the host, one by one"),
         "config": {"workload": w.name, "batch": w.batch, "prefill": w.prefill_lens[0], "q_heads": w.num_q_heads,
                    "kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block": 16, "r": w.r, "n_min": w.n_min,
                    "n_local": w.n_local, "f": w.f, "parallelism": "single GPU"},
