@@ -357,7 +357,8 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_rect_mfma(RectArgs a) {
     // page ids of the item's tiles (two per tile) and of the tiles requested
     // past the end (the last page repeated)
     const int page0 = key_lo / kBlock, last = (key_hi - 1) / kBlock;
-    const int nreq = (ntiles + NS - 1) / NS * NS + NS - 1;  // tiles the pipeline requests
+    // the pipeline reads the page ids of tiles up to one step past its last request
+    const int nreq = (ntiles + NS - 1) / NS * NS + NS;
     for (int i = tid; i < 2 * nreq; i += NT) pages[i] = checked_page(c, b, min(page0 + i, last));
 
     // this lane's query row as MFMA B operands (S^T = K Q^T)
@@ -381,11 +382,18 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_rect_mfma(RectArgs a) {
     const char* kbase = static_cast<const char*>(c.k) + size_t(g) * PAGE_BYTES;
     const char* vbase = static_cast<const char*>(c.v) + size_t(g) * PAGE_BYTES;
     const size_t pstride = size_t(c.Hkv) * PAGE_BYTES;
-    // Issue the LPT direct-to-LDS loads of tile ti into the given stage arrays.
-    auto issue_tile = [&](int ti, uint4* kst, uint4* vst) {
+    // The page ids of tile ti's LPT loads. In the loop they are read one step
+    // before the loads are issued, so that no step waits on an LDS round trip
+    // before its tile loads go out.
+    auto read_pages = [&](int ti, int (&pg)[LPT]) {
+#pragma unroll
+      for (int li = 0; li < LPT; ++li) pg[li] = pages[2 * ti + ld_ph[li]];
+    };
+    // Issue the LPT direct-to-LDS loads of a tile (page ids pg) into the given stage arrays.
+    auto issue_pages = [&](const int (&pg)[LPT], uint4* kst, uint4* vst) {
 #pragma unroll
       for (int li = 0; li < LPT; ++li) {
-        const int page = pages[2 * ti + ld_ph[li]];
+        const int page = pg[li];
         const bool isk = LPT >= 2 ? li < LPT / 2 : ld_k[li];
         const char* src = (isk ? kbase : vbase) + size_t(page) * pstride + ld_off[li];
         uint4* dst = (isk ? kst : vst) + ld_dst[li];
@@ -554,12 +562,16 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_rect_mfma(RectArgs a) {
     // is read, without adding waits of its own.
     f32x16_t s0, s1;
     static_for<0, NS - 1>([&](auto S) {
-      issue_tile(S.value, pick<S.value>(st0, st1, st2, st3, st4, st5, st6, st7),
-                 pick<S.value>(st0, st1, st2, st3, st4, st5, st6, st7) + PIECES);
+      int pg[LPT];
+      read_pages(S.value, pg);
+      issue_pages(pg, pick<S.value>(st0, st1, st2, st3, st4, st5, st6, st7),
+                  pick<S.value>(st0, st1, st2, st3, st4, st5, st6, st7) + PIECES);
     });
     wait_vmcnt<(NS - 2) * LPT>();
     asm volatile("s_barrier" ::: "memory");
     if (has_rows) score(s0, st0);
+    int pg_next[LPT];
+    read_pages(NS - 1, pg_next);
     for (int t0 = 0; t0 < ntiles; t0 += NS) {
       static_for<0, NS>([&](auto S) {
         const int t = t0 + S.value;
@@ -587,8 +599,9 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_rect_mfma(RectArgs a) {
           wait_lgkm0();
           asm volatile("s_barrier" ::: "memory");
         }
-        issue_tile(t + NS - 1, pick<SR>(st0, st1, st2, st3, st4, st5, st6, st7),
-                   pick<SR>(st0, st1, st2, st3, st4, st5, st6, st7) + PIECES);
+        issue_pages(pg_next, pick<SR>(st0, st1, st2, st3, st4, st5, st6, st7),
+                    pick<SR>(st0, st1, st2, st3, st4, st5, st6, st7) + PIECES);
+        read_pages(t + NS, pg_next);  // the next step's tile
         if (has_rows && t < ntiles) {
           if constexpr (S.value % 2 == 0)
             step_compute(t, s0, s1, pick<SN>(st0, st1, st2, st3, st4, st5, st6, st7),
