@@ -297,9 +297,11 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_rect_mfma(RectArgs a) {
   constexpr float kLazy = 8.0f;    // log2 units
   RESA_STAGE_DECL(0); RESA_STAGE_DECL(1); RESA_STAGE_DECL(2); RESA_STAGE_DECL(3);
   RESA_STAGE_DECL(4); RESA_STAGE_DECL(5); RESA_STAGE_DECL(6); RESA_STAGE_DECL(7);
-  __shared__ int pages[2 * (kMaxItemTiles + 2 * NS)];
+  __shared__ int2 tile_pages[kMaxItemTiles + 2 * NS];  // the two pages of each tile
   const CacheView& c = a.c;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is wave-uniform: from a scalar register, the per-wave
+  // load constants below and the tile-load addresses stay scalar
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
   const int G = c.G;
   const int item_begin = a.wg_first[blockIdx.x], item_end = a.wg_first[blockIdx.x + 1];
@@ -309,7 +311,7 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_rect_mfma(RectArgs a) {
   // the K stage and the rest the V stage, with one per thread the first half
   // of the waves take K.
   int ld_off[LPT];   // byte offset inside the page's K or V tile
-  int ld_ph[LPT];    // which of the tile's two pages
+  int ld_ph[LPT];    // which of the tile's two pages (wave-uniform)
   int ld_dst[LPT];   // first piece of the instruction in its stage array (wave-uniform)
   bool ld_k[LPT];    // wave-uniform; compile-time when LPT >= 2
 #pragma unroll
@@ -327,11 +329,11 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_rect_mfma(RectArgs a) {
       const int i = pidx / CPR, cp = (pidx % CPR) ^ (i % CPR);
       const int kt = (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
       ld_off[li] = ((kt & 15) * D + cp * 8) * 2;
-      ld_ph[li] = kt >> 4;
+      ld_ph[li] = __builtin_amdgcn_readfirstlane(kt >> 4);  // a wave's rows share bit 4
     } else {
       const int q = pidx / D, ch = pidx % D;
       ld_off[li] = (ch * kBlock + 8 * (q & 1)) * 2;
-      ld_ph[li] = q >> 1;
+      ld_ph[li] = __builtin_amdgcn_readfirstlane(q >> 1);  // a wave's pieces share q
     }
     ld_dst[li] = ins * 64;
   }
@@ -359,7 +361,9 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_rect_mfma(RectArgs a) {
     const int page0 = key_lo / kBlock, last = (key_hi - 1) / kBlock;
     // the pipeline reads the page ids of tiles up to one step past its last request
     const int nreq = (ntiles + NS - 1) / NS * NS + NS;
-    for (int i = tid; i < 2 * nreq; i += NT) pages[i] = checked_page(c, b, min(page0 + i, last));
+    for (int i = tid; i < nreq; i += NT)
+      tile_pages[i] = make_int2(checked_page(c, b, min(page0 + 2 * i, last)),
+                                checked_page(c, b, min(page0 + 2 * i + 1, last)));
 
     // this lane's query row as MFMA B operands (S^T = K Q^T)
     bf16x8_t qreg[KSTEPS];
@@ -382,20 +386,22 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_rect_mfma(RectArgs a) {
     const char* kbase = static_cast<const char*>(c.k) + size_t(g) * PAGE_BYTES;
     const char* vbase = static_cast<const char*>(c.v) + size_t(g) * PAGE_BYTES;
     const size_t pstride = size_t(c.Hkv) * PAGE_BYTES;
-    // The page ids of tile ti's LPT loads. In the loop they are read one step
-    // before the loads are issued, so that no step waits on an LDS round trip
-    // before its tile loads go out.
-    auto read_pages = [&](int ti, int (&pg)[LPT]) {
-#pragma unroll
-      for (int li = 0; li < LPT; ++li) pg[li] = pages[2 * ti + ld_ph[li]];
-    };
-    // Issue the LPT direct-to-LDS loads of a tile (page ids pg) into the given stage arrays.
-    auto issue_pages = [&](const int (&pg)[LPT], uint4* kst, uint4* vst) {
+    // The two page ids of tile ti. In the loop they are read one step before
+    // the tile's loads are issued, so that no step waits on an LDS round trip
+    // before its loads go out.
+    auto read_pages = [&](int ti) { return tile_pages[ti]; };
+    // Issue the LPT direct-to-LDS loads of a tile (page ids pg) into the given
+    // stage arrays. Every lane of a wave-wide load reads the same page, so the
+    // page's address is scalar work and only the lane's 32-bit offset inside
+    // it is a vector operand.
+    auto issue_pages = [&](int2 pg, uint4* kst, uint4* vst) {
+      const int p0 = __builtin_amdgcn_readfirstlane(pg.x), p1 = __builtin_amdgcn_readfirstlane(pg.y);
 #pragma unroll
       for (int li = 0; li < LPT; ++li) {
-        const int page = pg[li];
         const bool isk = LPT >= 2 ? li < LPT / 2 : ld_k[li];
-        const char* src = (isk ? kbase : vbase) + size_t(page) * pstride + ld_off[li];
+        const char* pbase = (isk ? kbase : vbase) + size_t(ld_ph[li] ? p1 : p0) * pstride;
+        asm("" : "+s"(pbase));  // kept whole in scalar registers
+        const char* src = pbase + uint32_t(ld_off[li]);
         uint4* dst = (isk ? kst : vst) + ld_dst[li];
         __builtin_amdgcn_global_load_lds((global_ptr_t)src, (lds_ptr_t)dst, 16, 0, CPOL);
       }
@@ -407,23 +413,23 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_rect_mfma(RectArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
     float m = -__builtin_inff(), lsum = 0.f;
+    // kept beside m, changed only by a rescale: the exponent offset -m (0
+    // while m = -inf: such a row has seen only masked logits) and the raw
+    // logit above which the running max moves, (m + kLazy) / scale_log2
+    // (scale > 0)
+    float nm = 0.f, thr = -__builtin_inff();
 
     // S^T tile of one stage: lane holds keys 16 (r / 8) + 8 half + r % 8 of
     // query row `col` (tile-relative key order after the row permutation).
-    // The lane offsets pass through an empty asm at every use, so the compiler
-    // adds them to each stage's base where they are read instead of keeping a
-    // precomputed address per stage and k-step live across the loop.
+    // The lane offsets pass through an empty asm at the top of every pass of
+    // the pipelined loop, so the compiler adds them to each stage's base where
+    // they are read instead of keeping a precomputed address per stage and
+    // k-step live across the loop.
     auto score_operands = [&](bf16x8_t (&ak)[KSTEPS], const uint4* kst) {
-      uint32_t ko[KSTEPS];
-#pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        ko[ks] = koff_base[ks];
-        asm volatile("" : "+v"(ko[ks]));
-      }
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks)
         ak[ks] = __builtin_bit_cast(bf16x8_t,
-                                    *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(kst) + ko[ks]));
+                                    *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(kst) + koff_base[ks]));
     };
     auto score = [&](f32x16_t& acc, const uint4* kst) {
       bf16x8_t ak[KSTEPS];
@@ -444,11 +450,15 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_rect_mfma(RectArgs a) {
 #pragma unroll
       for (int t = 0; t < DT; ++t) o[t] *= alpha;
       m = mnew;
+      nm = m == -__builtin_inff() ? 0.f : -m;
+      thr = (m + kLazy) / a.scale_log2;
     };
 
+    // the logits are finite or -inf (masked), never NaN: the NaN-propagating
+    // maximum needs no quieting of its operands
     auto half_max = [&](float x) {
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-      return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      return __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     };
 
     // One pipeline step's work: the softmax of tile t (scores in sacc), the
@@ -473,13 +483,11 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_rect_mfma(RectArgs a) {
       }
       float mx = sacc[0];
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
-      const float tmax = half_max(mx) * a.scale_log2;
+      for (int r = 1; r < 16; ++r) mx = __builtin_elementwise_maximum(mx, sacc[r]);
+      const float hmax = half_max(mx);
       // the running max moves only when a logit exceeds it by more than 2^8;
       // numerator and denominator share every rescale
-      if (__builtin_amdgcn_ballot_w64(tmax > m + kLazy)) rescale(tmax);
-      // a row that has seen no key yet (m = -inf) has only masked logits here
-      const float nm = m == -__builtin_inff() ? 0.f : -m;
+      if (__builtin_amdgcn_ballot_w64(hmax > thr)) rescale(hmax * a.scale_log2);
       f32x16_t z;
 #pragma unroll
       for (int r = 0; r < 16; ++r) z[r] = 0.f;
@@ -562,17 +570,16 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_rect_mfma(RectArgs a) {
     // is read, without adding waits of its own.
     f32x16_t s0, s1;
     static_for<0, NS - 1>([&](auto S) {
-      int pg[LPT];
-      read_pages(S.value, pg);
-      issue_pages(pg, pick<S.value>(st0, st1, st2, st3, st4, st5, st6, st7),
+      issue_pages(read_pages(S.value), pick<S.value>(st0, st1, st2, st3, st4, st5, st6, st7),
                   pick<S.value>(st0, st1, st2, st3, st4, st5, st6, st7) + PIECES);
     });
     wait_vmcnt<(NS - 2) * LPT>();
     asm volatile("s_barrier" ::: "memory");
     if (has_rows) score(s0, st0);
-    int pg_next[LPT];
-    read_pages(NS - 1, pg_next);
+    int2 pg_next = read_pages(NS - 1);
     for (int t0 = 0; t0 < ntiles; t0 += NS) {
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) asm volatile("" : "+v"(koff_base[ks]));
       static_for<0, NS>([&](auto S) {
         const int t = t0 + S.value;
         constexpr int SN = (S.value + 1) % NS;       // stage of tile t + 1
@@ -601,7 +608,7 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_rect_mfma(RectArgs a) {
         }
         issue_pages(pg_next, pick<SR>(st0, st1, st2, st3, st4, st5, st6, st7),
                     pick<SR>(st0, st1, st2, st3, st4, st5, st6, st7) + PIECES);
-        read_pages(t + NS, pg_next);  // the next step's tile
+        pg_next = read_pages(t + NS);  // the next step's tile
         if (has_rows && t < ntiles) {
           if constexpr (S.value % 2 == 0)
             step_compute(t, s0, s1, pick<SN>(st0, st1, st2, st3, st4, st5, st6, st7),
