@@ -115,6 +115,40 @@ def test_small_schedules(case):
     _run_loop_parity(w)
 
 
+def _random_case(i):
+    """A seeded random schedule: dtype, group size, KV heads, head_dim, ragged
+    prefill lengths (one to a few hundred blocks), steps, f (0: never), n_min, r
+    and n_local drawn independently."""
+    g = np.random.default_rng(7000 + i)
+    dt = "bf16" if g.random() < 0.7 else "fp32"
+    G = int(g.choice([1, 2, 4, 8]))
+    Hkv = int(g.integers(1, 4))
+    d = int(g.choice([64, 128]))
+    B = int(g.integers(1, 5))
+    pre = tuple(int(x) for x in g.integers(1, 2600, size=B))
+    steps = int(g.integers(2, 9))
+    f = int(g.choice([0, 1, 2, 3, 4, 5, 8]))
+    n_min = int(g.integers(1, 20))
+    r = float(np.round(g.uniform(0.02, 0.6), 3))
+    n_local = int(g.integers(0, 3))
+    name = f"rand{i}_{dt}_b{B}_g{G}_kv{Hkv}_d{d}_f{f}"
+    return (name, dt, B, G * Hkv, Hkv, d, pre, steps, f, n_min, r, n_local)
+
+
+RANDOM = [_random_case(i) for i in range(16)]
+
+
+@pytest.mark.parametrize("case", RANDOM, ids=[c[0] for c in RANDOM])
+def test_random_schedules(case):
+    """Seeded random shapes and parameters through the whole step loop: every
+    step's append, descriptors, selection and decode, and every rectification,
+    against the oracle."""
+    name, dt, B, Hq, Hkv, d, pre, steps, f, n_min, r, n_local = case
+    w = W.Workload(name, dt, B, Hq, Hkv, d, pre, steps, f, n_min, r, n_local,
+                   tuple(max(0, min(3, (L // 16) - 1)) for L in pre), dt == "bf16", 7000 + len(name))
+    _run_loop_parity(w)
+
+
 @pytest.mark.parametrize("case", [SMALL[0], SMALL[7]], ids=["bf16_g4_d128", "bf16_no_local"])
 def test_small_schedules_unfused_append(case):
     """The same schedules with the append as its own call (resa_update_descriptors)
