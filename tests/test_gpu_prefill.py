@@ -29,6 +29,23 @@ CASES = [
 ]
 
 
+
+def _random_case(i):
+    """A seeded random prefill: dtype, group size, KV heads, head_dim, batch,
+    prompt length and chunk size drawn independently."""
+    g = np.random.default_rng(9000 + i)
+    dt = "bf16" if g.random() < 0.75 else "fp32"
+    G = int(g.choice([1, 2, 4, 8]))
+    Hkv = int(g.integers(1, 4))
+    d = int(g.choice([64, 128]))
+    B = int(g.integers(1, 4))
+    T = int(g.integers(20, 900))
+    chunk = int(g.choice([1, 7, 16, 33, 64, 100, 256]))
+    return (f"rand{i}_{dt}_b{B}_g{G}_kv{Hkv}_d{d}_T{T}_c{chunk}", dt, B, G * Hkv, Hkv, d, T, chunk)
+
+
+CASES += [_random_case(i) for i in range(8)]
+
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_chunked_prefill_matches_dense_causal(case):
     from block_sparse_attention_quest_amd.schedule import ChunkedPrefill
