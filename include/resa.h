@@ -27,7 +27,10 @@
  *  - Device-side preconditions (seq_lens[b] <= max_seq_len, block_table entries
  *    in [0, num_pages) for every block a sequence holds, seq_lens[b] >= 1 for
  *    selection and decoding, f <= seq_lens[b] for rectification) are the
- *    caller's; they are not checked.
+ *    caller's; the library as normally built does not check them. A build with
+ *    RESA_DEBUG_CHECKS defined checks them on the device: every call then waits
+ *    for its stream and returns RESA_ERR_INVALID if one failed (a call under
+ *    HIP graph capture leaves the report to the next uncaptured call).
  *  - Workspaces: each call takes a caller-owned workspace of at least the size
  *    its *_workspace_size() function returns. Its contents on entry do not
  *    matter and are dead on return, so one workspace may serve all calls issued
