@@ -131,6 +131,16 @@ def long_256k(**kw) -> Workload:
     return w.replace(**kw) if kw else w
 
 
+def longest(**kw) -> Workload:
+    """Batch 1, 32q/8kv, d 128, bf16, at the longest context the library takes:
+    a 524,256-token prefill and 32 decode steps end at 524,288 tokens, 32,768
+    blocks (f 32: the rectification after the last step covers the final 32)."""
+    L = 524288 - 32
+    w = Workload("gqa32x8_d128_bf16_b1_512k", "bf16", 1, 32, 8, 128, (L,), 32, 32,
+                 16, 0.1, 1, (_planted_count(L, 0.01, None),), True, 5)
+    return w.replace(**kw) if kw else w
+
+
 def rectify_mixed(**kw) -> Workload:
     """16 sequences, total lengths U{4096..65536} (including the f=64 rectified
     tokens), 32q/8kv, d 128, bf16; one rectification of 64 tokens each."""

@@ -70,8 +70,9 @@ def _samples(w, k=3):
     return sorted(picks)
 
 
-@pytest.mark.parametrize("make", [W.gqa_128k, W.llama8b_32k, W.long_256k, lambda: W.long_256k(r=0.05, f=64)],
-                         ids=["128k_b4", "32k_b8", "256k_b1", "256k_b1_r05_f64"])
+@pytest.mark.parametrize("make", [W.gqa_128k, W.llama8b_32k, W.long_256k, lambda: W.long_256k(r=0.05, f=64),
+                                  W.longest],
+                         ids=["128k_b4", "32k_b8", "256k_b1", "256k_b1_r05_f64", "512k_b1_longest"])
 def test_decode_and_rectify_sampled(make):
     from block_sparse_attention_quest_amd.schedule import ResaRunner
     w0 = make()
