@@ -104,6 +104,10 @@ SMALL = [
     ("fp32_g2_d64", "fp32", 2, 4, 2, 64, (600, 77), 4, 4, 4, 0.1, 1),
     ("fp32_g4_d64", "fp32", 2, 8, 2, 64, (260, 1030), 5, 5, 4, 0.1, 1),
     ("fp32_g8_d128", "fp32", 1, 16, 2, 128, (700,), 4, 4, 8, 0.1, 1),
+    # the most KV heads the library takes: num_kv_heads * head_dim = 4096
+    ("bf16_kv32_g2_d128", "bf16", 2, 64, 32, 128, (300, 77), 4, 2, 4, 0.1, 1),
+    ("fp32_kv64_g1_d64", "fp32", 1, 64, 64, 64, (200,), 3, 3, 2, 0.1, 1),
+    ("bf16_kv64_g4_d64", "bf16", 1, 256, 64, 64, (150,), 3, 3, 2, 0.2, 1),
 ]
 
 
