@@ -108,6 +108,9 @@ SMALL = [
     ("bf16_kv32_g2_d128", "bf16", 2, 64, 32, 128, (300, 77), 4, 2, 4, 0.1, 1),
     ("fp32_kv64_g1_d64", "fp32", 1, 64, 64, 64, (200,), 3, 3, 2, 0.1, 1),
     ("bf16_kv64_g4_d64", "bf16", 1, 256, 64, 64, (150,), 3, 3, 2, 0.2, 1),
+    # a large ragged batch: 300 sequences of 1 to 400 tokens
+    ("bf16_b300_ragged", "bf16", 300, 8, 2, 128,
+     tuple(int(x) for x in np.random.default_rng(300).integers(1, 401, size=300)), 3, 2, 2, 0.1, 1),
 ]
 
 
