@@ -385,7 +385,10 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_rect_mfma(RectArgs a) {
 
     const char* kbase = static_cast<const char*>(c.k) + size_t(g) * PAGE_BYTES;
     const char* vbase = static_cast<const char*>(c.v) + size_t(g) * PAGE_BYTES;
-    const size_t pstride = size_t(c.Hkv) * PAGE_BYTES;
+    // a page's stride, Hkv K (or V) tiles; Hkv * D <= 4096 keeps it within 32
+    // bits (at most 128 KiB), so a page's byte offset is one 32 x 32 -> 64-bit
+    // scalar product of the (non-negative) page id and the stride
+    const uint32_t pstride = uint32_t(c.Hkv) * PAGE_BYTES;
     // The two page ids of tile ti. In the loop they are read one step before
     // the tile's loads are issued, so that no step waits on an LDS round trip
     // before its loads go out.
@@ -395,11 +398,12 @@ __global__ __launch_bounds__(64 * NWV, 2) void k_rect_mfma(RectArgs a) {
     // page's address is scalar work and only the lane's 32-bit offset inside
     // it is a vector operand.
     auto issue_pages = [&](int2 pg, uint4* kst, uint4* vst) {
-      const int p0 = __builtin_amdgcn_readfirstlane(pg.x), p1 = __builtin_amdgcn_readfirstlane(pg.y);
+      const uint64_t o0 = uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(pg.x))) * pstride;
+      const uint64_t o1 = uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(pg.y))) * pstride;
 #pragma unroll
       for (int li = 0; li < LPT; ++li) {
         const bool isk = LPT >= 2 ? li < LPT / 2 : ld_k[li];
-        const char* pbase = (isk ? kbase : vbase) + size_t(ld_ph[li] ? p1 : p0) * pstride;
+        const char* pbase = (isk ? kbase : vbase) + (ld_ph[li] ? o1 : o0);
         asm("" : "+s"(pbase));  // kept whole in scalar registers
         const char* src = pbase + uint32_t(ld_off[li]);
         uint4* dst = (isk ? kst : vst) + ld_dst[li];
