@@ -38,7 +38,9 @@ def _workloads():
     return {"gqa_128k": W.gqa_128k, "llama8b_32k": W.llama8b_32k, "long_256k": W.long_256k,
             "long_256k_r05": lambda: W.long_256k(r=0.05), "long_256k_f64": lambda: W.long_256k(f=64),
             "long_256k_r05_f64": lambda: W.long_256k(r=0.05, f=64),
-            "tiny_fp32": W.tiny_fp32, "rectify_mixed": W.rectify_mixed, "prompt_32k": W.prompt_32k,
+            # the longest context, less room for the bench's up to 512 steps
+            "longest": lambda: W.longest(prefill_lens=(524288 - 512,)), "tiny_fp32": W.tiny_fp32, "rectify_mixed": W.rectify_mixed,
+            "prompt_32k": W.prompt_32k,
             "prompt_32k_c256": lambda: W.prompt_32k(f=256), "prompt_32k_c1024": lambda: W.prompt_32k(f=1024)}
 
 
