@@ -327,6 +327,54 @@ def test_decode_is_deterministic():
         assert torch.equal(a, b)
 
 
+def test_rectify_is_deterministic():
+    """Two runs of one schedule with rectifications give bit-identical decode
+    and rectification outputs, cache rows and descriptors (no reduction in the
+    path uses atomics or a data-dependent order)."""
+    w = W.Workload("det_rect", "bf16", 3, 8, 2, 128, (900, 3000, 77), 6, 3, 16, 0.1, 1, (3, 3, 2), True, 11)
+    runs = []
+    for _ in range(2):
+        r = _runner(w)
+        res = []
+        for t in range(w.steps):
+            res.append(r.decode_step(t).clone())
+            if (t + 1) % w.f == 0:
+                rq, rk, rv = W.rectify_inputs(w, t)
+                res.append(r.rectify(t, rq.cuda(), rk.cuda(), rv.cuda()).clone())
+        torch.cuda.synchronize()
+        res += [r.cache.k_pages.clone(), r.cache.v_pages.clone(), r.cache.desc.clone()]
+        runs.append(res)
+    for a, b in zip(*runs):
+        assert torch.equal(a, b)
+
+
+def test_rebuilt_descriptors_equal_the_incremental_ones():
+    """Resume: after decode steps (one appended token each) and rectifications,
+    rebuilding every descriptor from the cached keys (resa_update_descriptors
+    with n_new = 0, what a restart from saved K/V pages does) gives exactly the
+    set the steps maintained."""
+    from block_sparse_attention_quest_amd import resa as R
+    w = W.Workload("resume", "bf16", 3, 8, 2, 128, (40, 1500, 333), 7, 3, 16, 0.1, 1, (1, 3, 3), True, 13)
+    r = _runner(w)
+    for t in range(w.steps):
+        r.decode_step(t)
+        if (t + 1) % w.f == 0:
+            rq, rk, rv = W.rectify_inputs(w, t)
+            r.rectify(t, rq.cuda(), rk.cuda(), rv.cuda())
+    torch.cuda.synchronize()
+    held = []
+    for b in range(w.batch):
+        M = -(-(w.prefill_lens[b] + w.steps) // 16)
+        held += r.block_table_cpu[b, :M].tolist()
+    held = torch.tensor(held, dtype=torch.long, device="cuda")
+    incremental = r.cache.desc[held].clone()
+    r.cache.desc[held] = float("nan")
+    r.set_step_lens(w.steps)
+    R.resa_update_descriptors(r.cache, None, None, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(r.cache.desc[held], incremental)
+
+
 def test_calls_from_two_host_threads_on_two_streams():
     """The library keeps no mutable state but the thread-local error text: two
     host threads, each with its own stream, workspace and outputs, select and
