@@ -148,3 +148,14 @@ def test_rectify_mixed_sampled():
                 err = P.out_error(P.f64(got[b, i, h]), ref, "bf16")
                 assert err <= P.ATOL["bf16"], (b, i, h, err)
         print(f"[result] group {(b, g)} (L={L}) ok", flush=True)
+
+
+def test_skewed_batch_longest_next_to_tiny_sequences():
+    """One sequence at the longest context beside a 5-token and a 300-token one:
+    the decode's splits and the rectification's plan are sized by the longest,
+    most of the short sequences' splits are empty. The whole step loop, every
+    descriptor and every rectification against the oracle."""
+    from test_gpu_parity import _run_loop_parity
+    L = 524288 - 3
+    w = W.Workload("skewed_512k_5_300", "bf16", 3, 4, 1, 64, (L, 5, 300), 3, 2, 16, 0.1, 1, (3, 0, 3), True, 23)
+    _run_loop_parity(w)
