@@ -205,3 +205,19 @@ def test_noalloc_decode_rejects_a_configuration_beyond_its_scratch(lib):
     st = lib.resa_sparse_decode_noalloc(ctypes.byref(c), None, ctypes.c_void_p(0x7000), ctypes.c_void_p(0x8000), 16,
                                         ctypes.c_float(0.1), ctypes.c_void_p(0x9000), None)
     assert st == R.RESA_ERR_INVALID
+
+
+def test_size_limits_are_exact(lib):
+    """The build's limits, on both sides: 32768 blocks per sequence and
+    num_kv_heads * head_dim = 4096 are taken (the host-only size queries
+    answer), one more block or twice the heads is not."""
+    ok = _cache(max_blocks_per_seq=32768, max_seq_len=524288, num_pages=32768 * 2)
+    assert lib.resa_select_workspace_size(ctypes.byref(ok)) > 0
+    assert lib.resa_n_cap(ctypes.byref(ok), ctypes.byref(R.ResaSelectParams(16, 1, 0.1))) == 3277
+    over = _cache(max_blocks_per_seq=32769, max_seq_len=524288, num_pages=32769 * 2)
+    assert lib.resa_select_workspace_size(ctypes.byref(over)) == 0
+    heads_ok = _cache(num_q_heads=32, num_kv_heads=32, head_dim=128)
+    assert lib.resa_select_workspace_size(ctypes.byref(heads_ok)) > 0
+    heads_over = _cache(num_q_heads=64, num_kv_heads=64, head_dim=128)
+    assert lib.resa_select_workspace_size(ctypes.byref(heads_over)) == 0
+    assert "4096" in lib.resa_last_error().decode()
