@@ -79,7 +79,7 @@ typedef enum { RESA_FP32 = 0, RESA_BF16 = 1 } resa_dtype;
  * dtype: q, K, V, descriptors and outputs share it. head_dim in {64, 128};
  * num_q_heads = G * num_kv_heads with group size G in {1, 2, 4, 8};
  * block_size must be 16 (the page size is the selection block).
- * Limits of this build, RESA_ERR_UNSUPPORTED beyond them: max_blocks_per_seq
+ * Limits of the library, RESA_ERR_UNSUPPORTED beyond them: max_blocks_per_seq
  * <= 32768 (524,288 tokens per sequence) and num_kv_heads * head_dim <= 4096.
  */
 typedef struct resa_cache {
